@@ -1,0 +1,6 @@
+"""KVarN KV-cache tile codec for AMD Instinct MI355X (gfx950).
+
+The codec runs as hand-written HIP kernels behind the C ABI declared in
+``include/kvarn.h`` (``libkvarn.so``); :mod:`.kvarn` is the thin Python binding
+and :mod:`.synth` generates seeded synthetic inputs.
+"""

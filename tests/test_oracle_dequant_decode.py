@@ -1,0 +1,174 @@
+"""Pins of the oracle's dequantiser and decode attention.
+
+Dequantisation applies the second scale with one extra multiply per element and
+undoes the rotation (paperlayer.ai summary of arXiv 2606.03458v1, section 3
+Methods and appendix I KVarN Dequantization Overhead).  Decode attention reads
+the packed cache at attention time (appendix I; dimensionstp review 4-2).
+"""
+import numpy as np
+import pytest
+import scipy.special
+
+from helpers import N, hadamard_ref, tiles_bits
+from kv_cache_quantization_x128_amd import synth
+
+K, V = 0, 1
+
+
+def _blank_record(orc, bits):
+    return np.zeros((1, orc.record_bytes(bits)), np.uint8)
+
+
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_single_code_closed_form(orc, axis, bits):
+    """One non-zero code: the dequantised tile is s2*code*s1 times one row of H."""
+    rec = _blank_record(orc, bits)
+    t0, c0, code = 37, 90, 2 ** bits - 1
+    byte = 16 * bits * t0 + (c0 * bits) // 8
+    rec[0, byte] |= code << ((c0 * bits) % 8)
+    base = 2048 * bits
+    g1, g2 = (c0, t0) if axis == K else (t0, c0)
+    rec[0, base + g1] = 0x3C       # s1 = 1.5
+    rec[0, base + 128 + g2] = 0x40  # s2 = 2.0 (other s2 = 0, other z = 0)
+    out = orc.dequantize(rec, bits, axis)[0]
+    exp = np.zeros((N, N))
+    exp[t0] = 2.0 * code * 1.5 * hadamard_ref()[c0]
+    assert np.array_equal(out, exp) or np.abs(out - exp).max() < 1e-14
+
+
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_dequant_error_bound_and_isometry(orc, axis, bits):
+    """|Yh - Y| <= s2 (s1/2 + L max(0, s1_pre - s1) + |z - mn|) per element, and
+    ||Xh_t - X_t|| = ||Yh_t - Y_t|| per token (H orthonormal)."""
+    k, v = synth.tiny(seed=55)
+    tiles = tiles_bits(k if axis == K else v)[:4]
+    view = orc.TileView.dense(tiles, orc.DT_F16)
+    rec, dbg = orc.quantize(view, bits, axis, debug=True)
+    xh = orc.dequantize(rec, bits, axis)
+    yh = orc.dequantize(rec, bits, axis, rotate=False)
+    _, s1b, s2b, zb = orc.record_fields(rec, bits)
+    import torch
+
+    dec = lambda b: torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).double().numpy()  # noqa
+    L = 2 ** bits - 1
+    x = tiles.view(np.float16).astype(np.float64)
+    for n in range(len(tiles)):
+        s1, s2, z = dec(s1b[n]), dec(s2b[n]), zb[n].view(np.float16).astype(np.float64)
+        slack = s1 / 2 + L * np.maximum(0, dbg["s1_pre"][n] - s1) + np.abs(z - dbg["z_pre"][n])
+        bound = (s2[:, None] * slack[None, :]) if axis == K else (s2[None, :] * slack[:, None])
+        err = np.abs(yh[n] - dbg["y"][n])
+        assert np.all(err <= bound * (1 + 1e-12) + 1e-12)
+        assert np.allclose(np.linalg.norm(xh[n] - x[n], axis=1), np.linalg.norm(yh[n] - dbg["y"][n], axis=1),
+                           rtol=1e-10, atol=1e-12)
+        assert np.abs(yh[n] @ hadamard_ref() - xh[n]).max() < 1e-12 * np.abs(xh[n]).max()
+
+
+def test_roundtrip_reduces_error_vs_kivi(orc):
+    """Sanity of the whole codec on the outlier model: the rotated+normalised code
+    reconstructs K better than plain per-channel RTN at the same 2 bits."""
+    k, _ = synth.tiny(seed=77)
+    tiles = tiles_bits(k)
+    x = tiles.view(np.float16).astype(np.float64)
+    view = orc.TileView.dense(tiles, orc.DT_F16)
+    e_kvarn = np.mean((orc.dequantize(orc.quantize(view, 2, K), 2, K) - x) ** 2)
+    e_kivi = np.mean((orc.dequantize(orc.quantize(view, 2, K, n_iter=0, rotate=False), 2, K, rotate=False) - x) ** 2)
+    assert e_kvarn < e_kivi
+
+
+# ----------------------------------------------------------------------------- decode attention
+def _cache(orc, n_seq, n_kv, n_tiles, seed, bits_k=2, bits_v=2, f=None):
+    rng = np.random.default_rng(seed)
+    kx = rng.standard_normal((n_seq * n_kv * n_tiles, N, N)).astype(np.float16)
+    vx = rng.standard_normal((n_seq * n_kv * n_tiles, N, N)).astype(np.float16)
+    if f is not None:
+        kx, vx = f(kx, vx)
+    kr = orc.quantize(orc.TileView.dense(tiles_bits(kx), orc.DT_F16), bits_k, K)
+    vr = orc.quantize(orc.TileView.dense(tiles_bits(vx), orc.DT_F16), bits_v, V)
+    return kr, vr
+
+
+def _brute(orc, q, kr, vr, n_tiles, hq, hkv, max_tiles, bk, bv, block_table=None):
+    """Decode attention from the oracle's own dequantised tiles with scipy's softmax."""
+    kd = orc.dequantize(kr, bk, K).astype(np.float16).astype(np.float64)
+    vd = orc.dequantize(vr, bv, V).astype(np.float16).astype(np.float64)
+    gs = hq // hkv
+    out = np.zeros((q.shape[0], hq, N))
+    for b in range(q.shape[0]):
+        for h in range(hq):
+            kvh = h // gs
+            rows = [(b * hkv + kvh) * max_tiles + j for j in range(min(n_tiles[b], max_tiles))]
+            if not rows:
+                continue
+            idx = [block_table[r] if block_table is not None else r for r in rows]
+            kk = kd[idx].reshape(-1, N)
+            vv = vd[idx].reshape(-1, N)
+            qq = q[b, h].astype(np.float64)
+            p = scipy.special.softmax(kk @ qq / np.sqrt(N))
+            out[b, h] = p @ vv
+    return out
+
+
+def test_decode_matches_brute_force_gqa_ragged(orc):
+    n_seq, hkv, hq, max_tiles = 3, 2, 8, 3
+    kr, vr = _cache(orc, n_seq, hkv, max_tiles, seed=5)
+    q = np.random.default_rng(6).standard_normal((n_seq, hq, N)).astype(np.float16)
+    n_tiles = np.array([3, 1, 2], np.int32)
+    got = orc.decode_attn(q.view(np.uint16), kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2)
+    ref = _brute(orc, q, kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2)
+    assert np.abs(got - ref).max() < 1e-12 * np.abs(ref).max()
+
+
+def test_decode_block_table_and_empty_sequence(orc):
+    n_seq, hkv, hq, max_tiles = 2, 1, 4, 2
+    kr, vr = _cache(orc, n_seq, hkv, max_tiles, seed=8, bits_k=4)
+    perm = np.array([3, 0, 2, 1], np.int32)          # record j of the table lives at perm[j]
+    kp = np.empty_like(kr)
+    vp = np.empty_like(vr)
+    kp[perm] = kr
+    vp[perm] = vr
+    q = np.random.default_rng(9).standard_normal((n_seq, hq, N)).astype(np.float16)
+    nt = np.array([2, 0], np.int32)
+    a = orc.decode_attn(q.view(np.uint16), kr, vr, nt, hq, hkv, max_tiles, 4, 2)
+    b = orc.decode_attn(q.view(np.uint16), kp, vp, nt, hq, hkv, max_tiles, 4, 2, block_table=perm)
+    assert np.array_equal(a, b)
+    assert not a[1].any()  # a sequence without tiles gets zeros
+
+
+def test_decode_constant_keys_give_mean_value(orc):
+    """All keys equal: uniform attention, the output is the mean of the dequantised values."""
+    def const_k(kx, vx):
+        kx[:] = np.float16(0.5)
+        return kx, vx
+
+    kr, vr = _cache(orc, 1, 1, 2, seed=11, f=const_k)
+    q = np.random.default_rng(12).standard_normal((1, 2, N)).astype(np.float16)
+    got = orc.decode_attn(q.view(np.uint16), kr, vr, np.array([2], np.int32), 2, 1, 2, 2, 2)
+    vd = orc.dequantize(vr, 2, V).astype(np.float16).astype(np.float64).reshape(-1, N)
+    assert np.abs(got[0] - vd.mean(0)).max() < 1e-12
+
+
+def test_decode_peaked_query_selects_planted_token(orc):
+    """A key aligned with the query at a very large logit takes all the attention weight."""
+    def plant(kx, vx):
+        kx[0, 77] = np.float16(0)
+        kx[0, 77, :8] = np.float16(60.0)
+        return kx, vx
+
+    kr, vr = _cache(orc, 1, 1, 1, seed=13, f=plant)
+    q = np.zeros((1, 1, N), np.float16)
+    q[0, 0, :8] = 30.0
+    got = orc.decode_attn(q.view(np.uint16), kr, vr, np.array([1], np.int32), 1, 1, 1, 2, 2)
+    vd = orc.dequantize(vr, 2, V).astype(np.float16).astype(np.float64)[0]
+    assert np.abs(got[0, 0] - vd[77]).max() < 1e-6 * np.abs(vd[77]).max()
+
+
+def test_rotated_domain_identity(orc):
+    """(H q) . Yh_t = q . Xh_t: attention can be scored without undoing the rotation."""
+    kr, _ = _cache(orc, 1, 1, 1, seed=14)
+    xh = orc.dequantize(kr, 2, K)[0]
+    yh = orc.dequantize(kr, 2, K, rotate=False)[0]
+    q = np.random.default_rng(15).standard_normal(N)
+    h = hadamard_ref()
+    assert np.allclose(yh @ (h @ q), xh @ q, rtol=1e-12, atol=1e-12)

@@ -1,0 +1,324 @@
+"""Pins of the oracle's quantiser against closed forms, invariants, library routines
+and brute force -- never against a re-typed copy of its own formulas.
+
+Method (arXiv 2606.03458, "KVarN"): Hadamard rotation over head_dim, then
+dual-axis std normalisation, then asymmetric round-to-nearest with FP8 group
+scales and an FP16 zero-point per 128 elements (paperlayer.ai summary, sections
+2 Preliminaries, 3 Methods, appendix D; agihunt.info note, pipeline paragraph).
+"""
+import numpy as np
+import pytest
+
+from helpers import N, hadamard_ref, nearest_fp8, rel_spread, tiles_bits
+from kv_cache_quantization_x128_amd import synth
+
+K, V = 0, 1
+
+
+@pytest.fixture(scope="module")
+def tiny_tiles():
+    k, v = synth.tiny()
+    return tiles_bits(k), tiles_bits(v)
+
+
+# ----------------------------------------------------------------------------- rotation
+def test_hadamard_is_scipy_sylvester(orc):
+    h = orc.hadamard()
+    assert np.array_equal(h, hadamard_ref())
+    assert np.abs(h @ h.T - np.eye(N)).max() < 1e-15
+    assert np.array_equal(h, h.T)
+
+
+def test_rotated_tile_is_x_times_h(orc, tiny_tiles):
+    kt, _ = tiny_tiles
+    view = orc.TileView.dense(kt[:2], orc.DT_F16)
+    _, dbg = orc.quantize(view, 2, K, debug=True)
+    x = kt[:2].view(np.float16).astype(np.float64)
+    y_ref = x @ hadamard_ref()
+    assert np.abs(dbg["y"] - y_ref).max() <= 1e-12 * np.abs(y_ref).max()
+    # orthonormal: every token keeps its norm
+    assert np.allclose(np.linalg.norm(dbg["y"], axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- normalisation
+def _normalised(y, r, c):
+    return y / r[:, None] / c[None, :]
+
+
+def test_sinkhorn_equalises_both_axes(orc, tiny_tiles):
+    """After eight iterations the stds are equal within each axis (spec bar 1e-3)."""
+    kt, vt = tiny_tiles
+    h = hadamard_ref()
+    worst = 0.0
+    for tile in list(kt) + list(vt):
+        y = tile.view(np.float16).astype(np.float64) @ h
+        r, c = orc.sinkhorn(y, 8)
+        z = _normalised(y, r, c)
+        row_sd = z.std(axis=1)  # numpy population std (ddof=0), centred
+        col_sd = z.std(axis=0)
+        assert rel_spread(row_sd) < 1e-12  # the last step is the token step
+        worst = max(worst, rel_spread(col_sd))
+    assert worst < 1e-3
+    assert worst < 1e-5  # what the iteration actually reaches on these tiles
+
+
+def test_sinkhorn_separable_matrix_closed_form(orc):
+    """Y_ij = a_i b_j (-1)^(i+j): one iteration gives r ∝ a and c ∝ b exactly."""
+    rng = np.random.default_rng(3)
+    a = np.exp(rng.normal(0, 1, N))
+    b = np.exp(rng.normal(0, 1, N))
+    sgn = (-1.0) ** np.add.outer(np.arange(N), np.arange(N))
+    y = a[:, None] * b[None, :] * sgn
+    for t in (1, 2, 8):
+        r, c = orc.sinkhorn(y, t)
+        assert rel_spread(r / a) < 1e-12
+        assert rel_spread(c / b) < 1e-12
+    # balanced +-1 matrix is a fixed point with r = c = 1
+    r, c = orc.sinkhorn(sgn, 5)
+    assert np.allclose(r, 1.0, rtol=1e-14) and np.allclose(c, 1.0, rtol=1e-14)
+
+
+def test_sinkhorn_equivariance(orc, tiny_tiles):
+    """diag(alpha) Y diag(beta): r scales by alpha and c by beta, up to one common factor."""
+    kt, _ = tiny_tiles
+    y = kt[3].view(np.float16).astype(np.float64) @ hadamard_ref()
+    rng = np.random.default_rng(4)
+    al = np.exp(rng.normal(0, 0.7, N))
+    be = np.exp(rng.normal(0, 0.7, N))
+    r0, c0 = orc.sinkhorn(y, 30)
+    r1, c1 = orc.sinkhorn(al[:, None] * y * be[None, :], 30)
+    assert rel_spread(r1 / (al * r0)) < 1e-6
+    assert rel_spread(c1 / (be * c0)) < 1e-6
+
+
+def test_degenerate_std_is_one(orc):
+    y = np.zeros((N, N))
+    r, c = orc.sinkhorn(y, 8)
+    assert np.all(r == 1.0) and np.all(c == 1.0)
+
+
+def test_degenerate_columns_ignore_rounding_noise(orc):
+    """Columns that are constant up to rounding noise behave like exactly constant ones:
+    the factors do not depend on the noise (relative degenerate floor)."""
+    rng = np.random.default_rng(5)
+    y = np.zeros((N, N))
+    y[:, :64] = rng.standard_normal((N, 64))
+    y[:, 64] = 3.0                                  # exactly constant column
+    noisy = y.copy()
+    noisy[:, 65:] = rng.standard_normal((N, 63)) * 1e-12
+    r0, c0 = orc.sinkhorn(y, 8)
+    r1, c1 = orc.sinkhorn(noisy, 8)
+    assert np.allclose(r0, r1, rtol=1e-9)
+    assert np.allclose(c0[:65], c1[:65], rtol=1e-9)
+
+
+# ----------------------------------------------------------------------------- RTN and metadata
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_codes_are_brute_force_nearest_levels(orc, tiny_tiles, axis, bits):
+    """Every code minimises |Zn - (code*s1 + z)| over all 2^b codes (ties to even)."""
+    tiles = tiny_tiles[axis][:4]
+    view = orc.TileView.dense(tiles, orc.DT_F16)
+    rec, dbg = orc.quantize(view, bits, axis, debug=True)
+    codes = orc.unpack_codes(rec, bits).astype(np.int64)
+    _, s1b, s2b, zb = orc.record_fields(rec, bits)
+    import torch
+
+    dec = lambda b: torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).double().numpy()  # noqa
+    s1, s2, z = dec(s1b), dec(s2b), zb.view(np.float16).astype(np.float64)
+    L = 2 ** bits - 1
+    levels = np.arange(L + 1)
+    for n in range(len(tiles)):
+        y = dbg["y"][n]
+        if axis == K:
+            zn = y / s2[n][:, None]
+            lv = levels[None, None, :] * s1[n][None, :, None] + z[n][None, :, None]
+        else:
+            zn = y / s2[n][None, :]
+            lv = levels[None, None, :] * s1[n][:, None, None] + z[n][:, None, None]
+        d = np.abs(zn[..., None] - lv)
+        best = d.argmin(-1)
+        tie = np.sort(d, -1)[..., 1] - d.min(-1) <= 1e-12 * np.abs(zn)
+        ok = (best == codes[n]) | (tie & (codes[n] % 2 == 0))
+        assert ok.all(), (n, np.argwhere(~ok)[:5])
+
+
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_metadata_follows_definitions(orc, tiny_tiles, axis, bits):
+    """s2 = nearest FP8 of a power-of-two multiple of the Sinkhorn factor with mean in [0.5, 1);
+    z = numpy float16 of the group min; s1 = nearest FP8 of (max - min) / L."""
+    tiles = tiny_tiles[axis][:3]
+    view = orc.TileView.dense(tiles, orc.DT_F16)
+    rec, dbg = orc.quantize(view, bits, axis, debug=True)
+    _, s1b, s2b, zb = orc.record_fields(rec, bits)
+    import torch
+
+    dec = lambda b: torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).double().numpy()  # noqa
+    for n in range(len(tiles)):
+        y = dbg["y"][n]
+        r, c = orc.sinkhorn(y, 8)
+        g = r if axis == K else c
+        ratio = dbg["g_pre"][n] / g
+        assert rel_spread(ratio) < 1e-14
+        assert np.log2(ratio[0]) == round(np.log2(ratio[0]))  # a power of two
+        assert 0.5 <= dbg["g_pre"][n].mean() < 1.0
+        s2 = dec(s2b[n])
+        assert np.array_equal(s2, nearest_fp8(dbg["g_pre"][n]))
+        zn = y / s2[:, None] if axis == K else y / s2[None, :]
+        gmin = zn.min(axis=0) if axis == K else zn.min(axis=1)
+        gmax = zn.max(axis=0) if axis == K else zn.max(axis=1)
+        assert np.array_equal(zb[n].view(np.float16), gmin.astype(np.float16))
+        assert np.array_equal(dec(s1b[n]), nearest_fp8((gmax - gmin) / (2 ** bits - 1)))
+
+
+def _grid_tile(rng, axis, bits, n_tiles):
+    """Tiles whose groups are exact grids m + k*d (d an FP8 value, m an FP16 value)."""
+    L = 2 ** bits - 1
+    k = rng.integers(0, L + 1, size=(n_tiles, N, N))
+    if axis == K:
+        k[:, 0, :], k[:, 1, :] = 0, L           # every channel spans the full grid
+    else:
+        k[:, :, 0], k[:, :, 1] = 0, L           # every token spans the full grid
+    _, fp8 = __import__("helpers").fp8_values()
+    fp8 = fp8[(fp8 >= 2.0 ** -4) & (fp8 <= 8.0)]
+    d = rng.choice(fp8, size=(n_tiles, N))
+    m = rng.uniform(-20, 20, size=(n_tiles, N)).astype(np.float16).astype(np.float64)
+    if axis == K:
+        x = m[:, None, :] + k * d[:, None, :]
+    else:
+        x = m[:, :, None] + k * d[:, :, None]
+    return k, d, m, x
+
+
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_kivi_special_case_exact(orc, axis, bits):
+    """No rotation, no normalisation: textbook per-channel (K) / per-token (V) min-max RTN.
+
+    With zero iterations the Sinkhorn factors are 1, the gauge makes s2 = 1/2,
+    so the stored scale is 2d, the zero-point 2m, the codes the grid indices
+    and dequantisation returns the input exactly (KIVI, paperlayer.ai summary
+    section 2 Preliminaries and section 5 Related Work).
+    """
+    rng = np.random.default_rng(10 + bits + axis)
+    k, d, m, x = _grid_tile(rng, axis, bits, 3)
+    xf = x.astype(np.float32)
+    assert np.array_equal(xf.astype(np.float64), x)
+    view = orc.TileView.dense(xf, orc.DT_F32)
+    rec = orc.quantize(view, bits, axis, n_iter=0, rotate=False)
+    codes = orc.unpack_codes(rec, bits)
+    assert np.array_equal(codes, k)
+    _, s1b, s2b, zb = orc.record_fields(rec, bits)
+    assert np.all(s2b == 0x30)  # FP8 0.5
+    import torch
+
+    s1 = torch.from_numpy(np.ascontiguousarray(s1b)).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(s1, 2 * d)
+    assert np.array_equal(zb.view(np.float16).astype(np.float64), 2 * m)
+    assert np.array_equal(orc.dequantize(rec, bits, axis, rotate=False), x)
+
+
+@pytest.mark.parametrize("axis", [K, V])
+def test_rotation_only_special_case(orc, axis):
+    """QuaRot-like mode (rotation, no normalisation): input G*H quantises to the grid G."""
+    bits = 2
+    rng = np.random.default_rng(20 + axis)
+    k, d, m, g = _grid_tile(rng, axis, bits, 2)
+    x = (g @ hadamard_ref()).astype(np.float32)
+    view = orc.TileView.dense(x, orc.DT_F32)
+    rec = orc.quantize(view, bits, axis, n_iter=0, rotate=True)
+    assert np.array_equal(orc.unpack_codes(rec, bits), k)
+    back = orc.dequantize(rec, bits, axis, rotate=True)
+    assert np.abs(back - x).max() < 1e-5 * np.abs(x).max()
+
+
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("shift", [-3, 2])
+def test_power_of_two_input_scaling(orc, tiny_tiles, axis, shift):
+    """x * 2^k: identical codes and s2; s1 and z scaled by exactly 2^k (scale absorption,
+    agihunt.info note: the normalisation coefficients go into the group scale)."""
+    tiles = tiny_tiles[axis][:3].view(np.float16).astype(np.float32)
+    bits = 2
+    r0 = orc.quantize(orc.TileView.dense(tiles, orc.DT_F32), bits, axis)
+    r1 = orc.quantize(orc.TileView.dense(tiles * np.float32(2.0 ** shift), orc.DT_F32), bits, axis)
+    c0, s10, s20, z0 = orc.record_fields(r0, bits)
+    c1, s11, s21, z1 = orc.record_fields(r1, bits)
+    assert np.array_equal(c0, c1)
+    assert np.array_equal(s20, s21)
+    import torch
+
+    dec = lambda b: torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).double().numpy()  # noqa
+    assert np.array_equal(dec(s11), dec(s10) * 2.0 ** shift)
+    assert np.array_equal(z1.view(np.float16).astype(np.float64), z0.view(np.float16).astype(np.float64) * 2.0 ** shift)
+
+
+def test_packing_layout(orc):
+    """Codes are token-major rows of 16*b bytes, channel c at bit c*b, LSB first."""
+    rng = np.random.default_rng(30)
+    for bits in (2, 4):
+        k, d, m, x = _grid_tile(rng, K, bits, 1)
+        rec = orc.quantize(orc.TileView.dense(x.astype(np.float32), orc.DT_F32), bits, K, n_iter=0,
+                           rotate=False)[0]
+        for t, c in [(0, 0), (0, 1), (5, 3), (17, 64), (127, 127), (64, 126)]:
+            byte = rec[16 * bits * t + (c * bits) // 8]
+            assert (byte >> ((c * bits) % 8)) & (2 ** bits - 1) == k[0, t, c]
+
+
+def test_constant_tile_reconstructs(orc):
+    """A constant tile rotates to one constant channel and 127 zero channels.  For K
+    every group (channel) is then constant, s1 falls to its 2^-9 floor and the codes
+    only absorb the FP16 rounding of z; for V every token is one spike whose top
+    level is clipped by L * (s1_pre - s1) when the FP8 scale rounds down."""
+    x = np.full((1, N, N), 0.75, np.float32)
+    for axis in (K, V):
+        rec = orc.quantize(orc.TileView.dense(x, orc.DT_F32), 2, axis)
+        _, s1b, _, _ = orc.record_fields(rec, 2)
+        if axis == K:
+            assert np.all(s1b == 0x01)  # FP8 2^-9
+        back = orc.dequantize(rec, 2, axis)
+        assert np.abs(back - 0.75).max() < (1e-3 if axis == K else 1e-2)
+
+
+def test_storage_accounting_matches_pages(orc):
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
+    elems = g["tile_shape"]["value"][0] * g["tile_shape"]["value"][1]
+    bits2 = orc.record_bytes(2) * 8 / elems
+    assert bits2 == g["effective_bits_2bit"]["value"]
+    half_up = lambda v: np.floor(v * 10 + 0.5) / 10  # noqa: E731  (the pages print 2.25 as "2.3")
+    assert half_up(bits2) == g["reported_bits_2bit"]["value"]
+    saving = 100 * (g["fp16_bits"]["value"] - g["reported_bits_2bit"]["value"]) / g["fp16_bits"]["value"]
+    assert round(saving, 1) == g["memory_reduction_percent"]["value"]
+    assert orc.record_bytes(4) * 8 / elems == 4.25
+    # one record per 128-token block: 2 FP8 scales + 1 FP16 zero per group of G = 128 elements
+    meta = orc.record_bytes(2) - 2 * elems // 8
+    assert meta == (1 + 1 + 2) * (elems // g["group_size"]["value"])
+
+
+def test_input_dtypes_and_strided_views_agree(orc):
+    """bf16, fp16 and fp32 inputs holding the same values, dense or strided through a
+    token-major [token][head][dim] buffer with per-tile offsets, give identical records."""
+    import torch
+
+    rng = np.random.default_rng(40)
+    vals = torch.from_numpy(rng.standard_normal((4, N, N)) * 3).to(torch.bfloat16)
+    f32 = vals.float().numpy()
+    bf = vals.view(torch.int16).numpy().view(np.uint16)
+    heads = 2
+    inter = np.zeros((2, N, heads, N), np.uint16)            # [seq][token][head][dim]
+    inter[0, :, 0], inter[0, :, 1], inter[1, :, 0], inter[1, :, 1] = bf[0], bf[1], bf[2], bf[3]
+    offs = np.array([0, N, N * heads * N, N * heads * N + N], np.int64)
+    strided = orc.TileView(inter.reshape(-1), orc.DT_BF16, 4, token_stride=heads * N, offsets=offs)
+    for axis in (K, V):
+        for bits in (2, 4):
+            a = orc.quantize(orc.TileView.dense(f32, orc.DT_F32), bits, axis)
+            b = orc.quantize(orc.TileView.dense(bf, orc.DT_BF16), bits, axis)
+            c = orc.quantize(strided, bits, axis)
+            assert np.array_equal(a, b) and np.array_equal(a, c)
+    h16 = f32.astype(np.float16)
+    a = orc.quantize(orc.TileView.dense(h16.astype(np.float32), orc.DT_F32), 2, K)
+    b = orc.quantize(orc.TileView.dense(h16.view(np.uint16), orc.DT_F16), 2, K)
+    assert np.array_equal(a, b)
