@@ -1,0 +1,246 @@
+"""Throughput of the KVarN codec on one MI355X.
+
+One step = quantise + dequantise the whole decode-append batch of the Qwen3-4B
+shape: 36 layers x 64 sequences x 8 KV heads, one new 128-token block each, K
+and V in bf16 laid out token-major [layer][seq][token][head][128] -- 18432 K
+tiles and 18432 V tiles, 2-bit.  Inputs are resident in HBM before timing.
+
+value = fp16-equivalent bytes moved by the step (36864 tiles x 32 KiB in the
+quantiser + the same out of the dequantiser) / step time.  The roofline object
+describes the dominant kernel (the quantiser): its algorithmic bytes per launch
+(tiles x (32768 + 4608)) over its HIP-event-timed average launch duration.
+Decode attention over the 2-bit cache (batch 16, 32 query heads on 8 KV heads,
+32768 tokens, 36 layers) is timed in the same run and reported in its own object.
+The oracle's quantise + dequantise is timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from kv_cache_quantization_x128_amd import kvarn, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+TILE_F16_BYTES = 128 * 128 * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class OpTimer:
+    """Accumulates HIP-event time of launches on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __call__(self, fn):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        torch.cuda.synchronize()
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
+
+
+def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2):
+    dev = torch.device("cuda:0")
+    log(f"generating decode-append inputs {layers}x{seqs}x128x{heads}x128 bf16")
+    k, v = synth.decode_append(n_layers=layers, n_seq=seqs, n_heads=heads, device=dev)
+    offs = synth.decode_append_offsets(layers, seqs, heads, device=dev)
+    n = offs.numel()
+    ts = heads * 128
+    pb = kvarn.tile_bytes(bits)
+    rk = torch.empty((n, pb), dtype=torch.uint8, device=dev)
+    rv = torch.empty_like(rk)
+    ok = torch.empty_like(k)
+    ov = torch.empty_like(v)
+    timers = {name: OpTimer() for name in ("quantize_k", "quantize_v", "dequantize_k", "dequantize_v")}
+
+    def step(timed):
+        ops = (
+            ("quantize_k", lambda: kvarn.quantize_tiles(k, n, bits, kvarn.AXIS_K, token_stride=ts, tile_offset=offs,
+                                                        out=rk)),
+            ("quantize_v", lambda: kvarn.quantize_tiles(v, n, bits, kvarn.AXIS_V, token_stride=ts, tile_offset=offs,
+                                                        out=rv)),
+            ("dequantize_k", lambda: kvarn.dequantize_tiles(rk, n, bits, kvarn.AXIS_K, ok, token_stride=ts,
+                                                            dst_offset=offs)),
+            ("dequantize_v", lambda: kvarn.dequantize_tiles(rv, n, bits, kvarn.AXIS_V, ov, token_stride=ts,
+                                                            dst_offset=offs)),
+        )
+        for name, fn in ops:
+            if timed:
+                timers[name](fn)
+            else:
+                fn()
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op = {name: t.mean_ms() for name, t in timers.items()}
+    return dict(n_tiles_per_cache=n, bits=bits, wall_s=wall, per_op_ms=per_op, record_bytes=pb)
+
+
+def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768, bits=2):
+    dev = torch.device("cuda:0")
+    nt = tokens // 128
+    g = synth.generator(1005, dev)
+    caches = []
+    log(f"building {layers} decode-attention layers (batch {batch}, {tokens} tokens)")
+    for _ in range(layers):
+        q, k, v = synth.decode_attn_layer(g, n_seq=batch, n_kv_heads=hkv, n_q_heads=hq, n_tokens=tokens, device=dev)
+        caches.append((q, kvarn.quantize(k, bits, kvarn.AXIS_K), kvarn.quantize(v, bits, kvarn.AXIS_V)))
+        del k, v
+    torch.cuda.empty_cache()
+    n_tiles = torch.full((batch,), nt, dtype=torch.int32, device=dev)
+    ws = torch.empty(kvarn.workspace_bytes(batch, hq, hkv, nt), dtype=torch.uint8, device=dev)
+    out = torch.empty((batch, hq, 128), dtype=torch.float16, device=dev)
+    timer = OpTimer()
+
+    def one_pass(timed):
+        for q, kr, vr in caches:
+            fn = lambda: kvarn.decode_attn(q, kr, vr, n_tiles, hkv, nt, bits, bits, out=out, workspace=ws)  # noqa
+            timer(fn) if timed else fn()
+
+    for _ in range(warmup):
+        one_pass(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        one_pass(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    layer_ms = timer.mean_ms()
+    pb = kvarn.tile_bytes(bits)
+    alg_bytes = 2 * batch * hkv * nt * pb + 2 * batch * hq * 128 * 2
+    ach = alg_bytes / (layer_ms * 1e-3) / 1e9
+    return {
+        "workload": f"decode attention: batch {batch}, {hq} query heads on {hkv} KV heads, head_dim 128, "
+                    f"{tokens}-token {bits}-bit K/V cache, {layers} layers",
+        "layer_ms": layer_ms,
+        "wall_s_per_pass": wall / passes,
+        "fp16_equiv_GBs": 2 * batch * hkv * nt * TILE_F16_BYTES / (layer_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": alg_bytes},
+        "tokens_per_s": batch * hq / (layer_ms * 1e-3),
+    }
+
+
+def cpu_baseline(target_s=15.0, bits=2):
+    """The oracle's quantise + dequantise on a bounded sample of decode-append K tiles."""
+    import oracle
+
+    per_layer = 64 * 8
+
+    def tiles(n_layers):
+        k = synth.decode_append(n_layers=n_layers, n_seq=64, n_heads=8, device="cpu")[0]
+        offs = synth.decode_append_offsets(n_layers, 64, 8, device="cpu").numpy()
+        return k.contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1), offs
+
+    def run(buf, offs, m):
+        view = oracle.TileView(buf, oracle.DT_BF16, m, token_stride=8 * 128, offsets=offs[:m])
+        t0 = time.perf_counter()
+        rec = oracle.quantize(view, bits, oracle.AXIS_K)
+        oracle.dequantize(rec, bits, oracle.AXIS_K)
+        return time.perf_counter() - t0
+
+    buf, offs = tiles(1)
+    probe = 64
+    dt = run(buf, offs, probe)
+    m = int(min(36 * per_layer, max(probe, probe * target_s / max(dt, 1e-3))))
+    n_layers = -(-m // per_layer)
+    if n_layers > 1:
+        buf, offs = tiles(n_layers)
+    dt = run(buf, offs, m)
+    return {"value": 2 * m * TILE_F16_BYTES / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{m} K tiles ({n_layers} layers) of the decode-append workload, quantise + dequantise, "
+                      f"{dt:.1f} s on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-passes", type=int, default=20)
+    ap.add_argument("--decode-layers", type=int, default=36)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the codec has no cross-GPU step); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    kvarn.load()
+    torch.cuda.init()
+
+    codec = bench_codec(args.steps, args.warmup)
+    n = codec["n_tiles_per_cache"]
+    per_op = codec["per_op_ms"]
+    step_ms = codec["wall_s"] / args.steps * 1e3
+    f16_bytes = 2 * (2 * n) * TILE_F16_BYTES          # quantiser reads + dequantiser writes, K and V
+    value = f16_bytes / (step_ms * 1e-3) / 1e9
+    pb = codec["record_bytes"]
+    q_ms = 0.5 * (per_op["quantize_k"] + per_op["quantize_v"])
+    dq_ms = 0.5 * (per_op["dequantize_k"] + per_op["dequantize_v"])
+    q_alg = n * (TILE_F16_BYTES + pb)
+    q_ach = q_alg / (q_ms * 1e-3) / 1e9
+    dq_ach = q_alg / (dq_ms * 1e-3) / 1e9
+    ops = {
+        "quantize": {"launch_ms": q_ms, "tiles_per_launch": n, "tiles_per_s": n / (q_ms * 1e-3),
+                     "algorithmic_GBs": q_ach, "frac_hbm": q_ach / HBM_PEAK_GBS,
+                     "fp16_equiv_GBs": n * TILE_F16_BYTES / (q_ms * 1e-3) / 1e9},
+        "dequantize": {"launch_ms": dq_ms, "tiles_per_launch": n, "tiles_per_s": n / (dq_ms * 1e-3),
+                       "algorithmic_GBs": dq_ach, "frac_hbm": dq_ach / HBM_PEAK_GBS,
+                       "fp16_equiv_GBs": n * TILE_F16_BYTES / (dq_ms * 1e-3) / 1e9},
+    }
+    line = {
+        "metric": "KV quantize+dequant GB/s (fp16-equiv) and % of HBM peak on 1 MI355X",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1), outlier channels x15, 5% outlier tokens x4, RoPE-rotated keys; bf16)",
+        "config": {"workload": "decode_append: Qwen3-4B KV shape, 36 layers x 64 sequences x 8 KV heads, one "
+                               "128-token block each, head_dim 128, bf16 K and V, 2-bit",
+                   "tiles_per_step": 2 * n, "layout": "[layer][seq][token][head][128]", "n_iter": 8},
+        "frac_of_hbm_peak": value / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": q_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": q_ach / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": q_alg},
+        "ops": ops,
+    }
+    if not args.no_decode:
+        line["decode_attn"] = bench_decode(args.decode_passes, 2, layers=args.decode_layers)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+// kvarn_api.hip -- the extern "C" entry points of libkvarn.so (declared in
+// include/kvarn.h).  Every argument is checked here, before any HIP call, so
+// that misuse is reported as a status code on any machine; the kernels then
+// run asynchronously on the caller's stream.
+#include <stdio.h>
+#include <string.h>
+
+#include "kvarn.h"
+#include "kvarn_launch.h"
+
+using kvarn::DecodeArgs;
+using kvarn::DequantizeArgs;
+using kvarn::QuantizeArgs;
+
+namespace {
+
+constexpr int64_t kMaxTilesPerLaunch = 0x7FFFFFFF;  // grid x limit
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_bits(int b) { return b == 2 || b == 4; }
+bool valid_dtype(int d) { return d == KVARN_F16 || d == KVARN_BF16 || d == KVARN_F32; }
+bool valid_axis(int a) { return a == KVARN_AXIS_K || a == KVARN_AXIS_V; }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return KVARN_OK;
+    fprintf(stderr, "libkvarn: HIP error %d (%s)\n", (int)e, hipGetErrorString(e));
+    return KVARN_EHIP;
+}
+
+// Shared checks of the tile addressing of quantize (input) and dequantize (output).
+int check_tiles(const void* buf, int64_t n_tiles, int64_t tile_stride, int64_t token_stride, const int64_t* offs) {
+    if (buf == nullptr || n_tiles < 0 || token_stride < KVARN_HEAD_DIM) return KVARN_EINVAL;
+    if (offs == nullptr && tile_stride < 0) return KVARN_EINVAL;
+    if (n_tiles > kMaxTilesPerLaunch) return KVARN_EINVAL;
+    if (!aligned16(buf)) return KVARN_EALIGN;
+    if ((token_stride & 7) != 0 || (offs == nullptr && (tile_stride & 7) != 0)) return KVARN_EALIGN;
+    if (offs != nullptr && (reinterpret_cast<uintptr_t>(offs) & 7u) != 0) return KVARN_EALIGN;
+    return KVARN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvarn_format_version(void) { return KVARN_FORMAT_VERSION; }
+
+size_t kvarn_tile_bytes(int bits) { return valid_bits(bits) ? (size_t)(2048 * bits + 512) : 0; }
+
+const char* kvarn_status_string(int status) {
+    switch (status) {
+    case KVARN_OK: return "ok";
+    case KVARN_EINVAL: return "invalid argument";
+    case KVARN_EUNSUPPORTED: return "unsupported configuration";
+    case KVARN_EALIGN: return "misaligned pointer or stride";
+    case KVARN_EWORKSPACE: return "workspace too small";
+    case KVARN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int kvarn_parse_preset(const char* preset, int* bits_k, int* bits_v, int* group) {
+    if (preset == nullptr || bits_k == nullptr || bits_v == nullptr || group == nullptr) return KVARN_EINVAL;
+    int bk = 0, bv = 0, g = 0, used = 0;
+    if (sscanf(preset, "kvarn_k%dv%d_g%d%n", &bk, &bv, &g, &used) != 3 || preset[used] != '\0') return KVARN_EINVAL;
+    if (!valid_bits(bk) || !valid_bits(bv) || g != 128) return KVARN_EUNSUPPORTED;
+    *bits_k = bk;
+    *bits_v = bv;
+    *group = g;
+    return KVARN_OK;
+}
+
+int kvarn_quantize_tiles(const void* x, int x_dtype, int64_t n_tiles, int64_t tile_stride, int64_t token_stride,
+                         const int64_t* tile_offset, int bits, int axis, int n_iter, void* packed,
+                         const int64_t* dst_tile_index, hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || !valid_axis(axis) || packed == nullptr || n_iter < 0 || n_iter > 64)
+        return KVARN_EINVAL;
+    if (!valid_bits(bits)) return KVARN_EUNSUPPORTED;
+    const int st = check_tiles(x, n_tiles, tile_stride, token_stride, tile_offset);
+    if (st != KVARN_OK) return st;
+    if (!aligned16(packed)) return KVARN_EALIGN;
+    if (dst_tile_index != nullptr && (reinterpret_cast<uintptr_t>(dst_tile_index) & 7u) != 0) return KVARN_EALIGN;
+    if (n_tiles == 0) return KVARN_OK;
+    QuantizeArgs a{x, x_dtype, n_tiles, tile_stride, token_stride, tile_offset, bits, axis, n_iter,
+                   static_cast<uint8_t*>(packed), dst_tile_index, stream};
+    return hip_status(kvarn::launch_quantize(a));
+}
+
+int kvarn_dequantize_tiles(const void* packed, const int64_t* src_tile_index, int64_t n_tiles, int bits, int axis,
+                           void* out, int out_dtype, int64_t tile_stride, int64_t token_stride,
+                           const int64_t* dst_tile_offset, hipStream_t stream) {
+    if (!valid_dtype(out_dtype) || !valid_axis(axis) || packed == nullptr) return KVARN_EINVAL;
+    if (!valid_bits(bits)) return KVARN_EUNSUPPORTED;
+    const int st = check_tiles(out, n_tiles, tile_stride, token_stride, dst_tile_offset);
+    if (st != KVARN_OK) return st;
+    if (!aligned16(packed)) return KVARN_EALIGN;
+    if (src_tile_index != nullptr && (reinterpret_cast<uintptr_t>(src_tile_index) & 7u) != 0) return KVARN_EALIGN;
+    if (n_tiles == 0) return KVARN_OK;
+    DequantizeArgs a{static_cast<const uint8_t*>(packed), src_tile_index, n_tiles, bits, axis, out, out_dtype,
+                     tile_stride, token_stride, dst_tile_offset, stream};
+    return hip_status(kvarn::launch_dequantize(a));
+}
+
+size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_heads, int max_tiles) {
+    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0) return 0;
+    int n_splits = 1, tps = 1;
+    kvarn::decode_split_plan(batch, n_kv_heads, max_tiles, &n_splits, &tps);
+    return (size_t)batch * (size_t)n_q_heads * (size_t)n_splits * (size_t)(2 + KVARN_HEAD_DIM) * sizeof(float);
+}
+
+int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
+                      const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
+                      int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, void* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (q == nullptr || k_packed == nullptr || v_packed == nullptr || n_tiles_per_seq == nullptr ||
+        out == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0 || n_records < 0 ||
+        n_q_heads % n_kv_heads != 0 || !(sm_scale == sm_scale))
+        return KVARN_EINVAL;
+    if (!valid_bits(bits_k) || !valid_bits(bits_v) || n_q_heads / n_kv_heads > 8) return KVARN_EUNSUPPORTED;
+    if (batch > 65535 || n_kv_heads > 65535) return KVARN_EUNSUPPORTED;  // grid y/z limits
+    if (!aligned16(q) || !aligned16(k_packed) || !aligned16(v_packed) || !aligned16(out)) return KVARN_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(n_tiles_per_seq) & 3u) != 0 ||
+        (block_table != nullptr && (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))
+        return KVARN_EALIGN;
+    if (batch == 0) return KVARN_OK;
+    const size_t need = kvarn_decode_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, max_tiles);
+    if (workspace == nullptr || workspace_bytes < need) return KVARN_EWORKSPACE;
+    if (!aligned16(workspace)) return KVARN_EALIGN;
+    DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_packed = static_cast<const uint8_t*>(k_packed);
+    a.v_packed = static_cast<const uint8_t*>(v_packed);
+    a.block_table = block_table;
+    a.n_tiles_per_seq = n_tiles_per_seq;
+    a.n_records = n_records;
+    a.batch = batch;
+    a.n_q_heads = n_q_heads;
+    a.n_kv_heads = n_kv_heads;
+    a.max_tiles = max_tiles;
+    a.bits_k = bits_k;
+    a.bits_v = bits_v;
+    a.sm_scale = sm_scale;
+    a.out = static_cast<uint16_t*>(out);
+    a.workspace = static_cast<float*>(workspace);
+    a.stream = stream;
+    kvarn::decode_split_plan(batch, n_kv_heads, max_tiles, &a.n_splits, &a.tiles_per_split);
+    return hip_status(kvarn::launch_decode(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// kvarn_device.h -- device-side helpers shared by the KVarN HIP kernels (gfx950).
+//
+// Number formats follow their public definitions: OCP 8-bit floating point
+// E4M3 (the "FN" variant, largest finite 448) for the two scales, IEEE binary16
+// for the zero-point, bfloat16 / binary16 / binary32 for tiles.  The record
+// layout is the one documented in include/kvarn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace kvarn {
+
+constexpr int kN = 128;                              // tokens per tile and head_dim
+constexpr float kInvSqrtN = 0.0883883476483184405f;  // 1/sqrt(128) rounded to fp32
+
+enum : int { kF16 = 0, kBF16 = 1, kF32 = 2 };
+enum : int { kAxisK = 0, kAxisV = 1 };
+
+template <int BITS>
+struct Rec {
+    static constexpr int kCodeBytes = 2048 * BITS;   // 128 tokens x 16*BITS bytes
+    static constexpr int kRowBytes = 16 * BITS;      // codes of one token
+    static constexpr int kS1 = kCodeBytes;           // FP8 group scales
+    static constexpr int kS2 = kCodeBytes + 128;     // FP8 second scales
+    static constexpr int kZ = kCodeBytes + 256;      // FP16 zero-points
+    static constexpr int kBytes = kCodeBytes + 512;
+    static constexpr int kL = (1 << BITS) - 1;
+};
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return __half2float(__ushort_as_half((unsigned short)h));
+}
+
+// Round to nearest even; inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Round to nearest even, saturating at +-65504.
+__device__ __forceinline__ uint32_t f32_to_f16_bits_sat(float f) {
+    f = fminf(fmaxf(f, -65504.0f), 65504.0f);
+    return (uint32_t)__half_as_ushort(__float2half_rn(f));
+}
+
+__device__ __forceinline__ float pow2f(int e) {  // 2^e for -126 <= e <= 127
+    return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+// FP8 E4M3 code of a non-negative finite v: round to nearest even, saturate at
+// 448 (code 0x7E).  Scaling by powers of two is exact, so every step is exact
+// except the final rint (v_rndne_f32).
+__device__ __forceinline__ uint32_t fp8_encode_nonneg(float v) {
+    const int e = (int)(__float_as_uint(v) >> 23) - 127;  // floor(log2 v) for normal v
+    if (e < -6) {                                          // subnormal grid, quantum 2^-9
+        return (uint32_t)__builtin_rintf(v * 512.0f);      // 0..8; 8 is the code of 2^-6
+    }
+    const float m = __builtin_rintf(v * pow2f(3 - e));     // 8..16
+    const uint32_t code = (uint32_t)((e + 7) << 3) + (uint32_t)m - 8u;
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Value of an FP8 E4M3 code with the sign bit clear (NaN code not used).
+__device__ __forceinline__ float fp8_decode_nonneg(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 0) return (float)m * (1.0f / 512.0f);
+    return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------------------- Walsh-Hadamard
+// In-register unnormalised fast Walsh-Hadamard transform of NV values
+// (natural / Sylvester order): butterfly (a, b) -> (a + b, a - b) over every
+// index bit.
+template <int NV>
+__device__ __forceinline__ void fwht_regs(float (&v)[NV]) {
+#pragma unroll
+    for (int s = 1; s < NV; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if ((i & s) == 0) {
+                const float a = v[i], b = v[i + s];
+                v[i] = a + b;
+                v[i + s] = a - b;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- lane reductions
+// Sum / max over the 16 lanes that differ in lane bits 0-3.
+__device__ __forceinline__ float sum_lanes16(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+__device__ __forceinline__ float max_lanes16(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+__device__ __forceinline__ float min_lanes16(float v) {
+    v = fminf(v, __shfl_xor(v, 1));
+    v = fminf(v, __shfl_xor(v, 2));
+    v = fminf(v, __shfl_xor(v, 4));
+    v = fminf(v, __shfl_xor(v, 8));
+    return v;
+}
+// Sum / max / min over the 4 lanes that differ in lane bits 4-5.
+__device__ __forceinline__ float sum_lanes_hi(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+__device__ __forceinline__ float max_lanes_hi(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float min_lanes_hi(float v) {
+    v = fminf(v, __shfl_xor(v, 16));
+    v = fminf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// ---------------------------------------------------------------- tile row I/O
+// Load 64 consecutive elements starting at element e0 of x as fp32.
+template <int DT>
+__device__ __forceinline__ void load64(const void* __restrict__ x, int64_t e0, bool vec, float (&v)[64]) {
+    if constexpr (DT == kF32) {
+        const float* p = reinterpret_cast<const float*>(x) + e0;
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float4 q = reinterpret_cast<const float4*>(p)[i];
+                v[4 * i] = q.x, v[4 * i + 1] = q.y, v[4 * i + 2] = q.z, v[4 * i + 3] = q.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 64; ++i) v[i] = p[i];
+        }
+    } else {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + e0;
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if constexpr (DT == kBF16) {
+                        v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+                        v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+                    } else {
+                        v[8 * i + 2 * k] = f16_bits_to_f32(w[k] & 0xFFFFu);
+                        v[8 * i + 2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 64; ++i)
+                v[i] = (DT == kBF16) ? bf16_bits_to_f32(p[i]) : f16_bits_to_f32(p[i]);
+        }
+    }
+}
+
+// Store 64 fp32 values to consecutive elements starting at e0 as DT.
+template <int DT>
+__device__ __forceinline__ void store64(void* __restrict__ out, int64_t e0, bool vec, const float (&v)[64]) {
+    if constexpr (DT == kF32) {
+        float* p = reinterpret_cast<float*>(out) + e0;
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 64; ++i) p[i] = v[i];
+        }
+    } else {
+        uint16_t* p = reinterpret_cast<uint16_t*>(out) + e0;
+        uint32_t h[64];
+#pragma unroll
+        for (int i = 0; i < 64; ++i) h[i] = (DT == kBF16) ? f32_to_bf16_bits(v[i]) : f32_to_f16_bits_sat(v[i]);
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint4 q;
+                q.x = h[8 * i] | (h[8 * i + 1] << 16);
+                q.y = h[8 * i + 2] | (h[8 * i + 3] << 16);
+                q.z = h[8 * i + 4] | (h[8 * i + 5] << 16);
+                q.w = h[8 * i + 6] | (h[8 * i + 7] << 16);
+                reinterpret_cast<uint4*>(p)[i] = q;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 64; ++i) p[i] = (uint16_t)h[i];
+        }
+    }
+}
+
+}  // namespace kvarn

@@ -1,0 +1,157 @@
+"""Python binding of libkvarn.so (the C ABI in include/kvarn.h).
+
+Argument marshalling only: every step of the codec runs in the HIP kernels of
+``libkvarn.so``.  PyTorch supplies device memory (``Tensor.data_ptr()``) and the
+stream (``torch.cuda.current_stream()``).  There is no fallback: if the library
+is missing, :func:`load` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvarn.so")
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
+F16, BF16, F32 = 0, 1, 2
+AXIS_K, AXIS_V = 0, 1
+HEAD_DIM = TILE = 128
+
+# Every function declared in include/kvarn.h, with its ctypes signature.
+_P, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+SIGNATURES = {
+    "kvarn_format_version": (_I, []),
+    "kvarn_tile_bytes": (_SZ, [_I]),
+    "kvarn_parse_preset": (_I, [ctypes.c_char_p, _P, _P, _P]),
+    "kvarn_status_string": (ctypes.c_char_p, [_I]),
+    "kvarn_quantize_tiles": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _P, _P, _P]),
+    "kvarn_dequantize_tiles": (_I, [_P, _P, _I64, _I, _I, _P, _I, _I64, _I64, _P, _P]),
+    "kvarn_decode_attn_workspace_bytes": (_SZ, [_I64, _I, _I, _I]),
+    "kvarn_decode_attn": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+class KvarnError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libkvarn.so (built by ``python -m kv_cache_quantization_x128_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_quantization_x128_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().kvarn_status_string(int(status)).decode()
+
+
+def tile_bytes(bits: int) -> int:
+    return int(load().kvarn_tile_bytes(bits))
+
+
+def format_version() -> int:
+    return int(load().kvarn_format_version())
+
+
+def parse_preset(preset: str):
+    bk, bv, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = load().kvarn_parse_preset(preset.encode(), ctypes.byref(bk), ctypes.byref(bv), ctypes.byref(g))
+    if st != OK:
+        raise KvarnError("kvarn_parse_preset", st)
+    return bk.value, bv.value, g.value
+
+
+def workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_tiles: int) -> int:
+    return int(load().kvarn_decode_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, max_tiles))
+
+
+# --------------------------------------------------------------------------- helpers
+_DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, st):
+    if st != OK:
+        raise KvarnError(fn, st)
+
+
+# --------------------------------------------------------------------------- entry points
+def quantize_tiles(x: torch.Tensor, n_tiles: int, bits: int, axis: int, *, tile_stride: int = TILE * HEAD_DIM,
+                   token_stride: int = HEAD_DIM, tile_offset: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None, dst_index: torch.Tensor | None = None, n_iter: int = 8,
+                   stream=None) -> torch.Tensor:
+    """Quantise tiles of ``x`` (fp16/bf16/fp32 on the GPU) into packed uint8 records [n, Pb]."""
+    if out is None:
+        out = torch.empty((n_tiles, tile_bytes(bits)), dtype=torch.uint8, device=x.device)
+    st = load().kvarn_quantize_tiles(_ptr(x), _DT[x.dtype], n_tiles, tile_stride, token_stride, _ptr(tile_offset),
+                                     bits, axis, n_iter, _ptr(out), _ptr(dst_index), _stream(stream))
+    _check("kvarn_quantize_tiles", st)
+    return out
+
+
+def quantize(x: torch.Tensor, bits: int, axis: int, n_iter: int = 8, stream=None) -> torch.Tensor:
+    """Dense ``x[..., T, 128]`` (T a multiple of 128, contiguous) -> records [x.numel() / 16384, Pb]."""
+    assert x.is_contiguous() and x.shape[-1] == HEAD_DIM and x.shape[-2] % TILE == 0
+    return quantize_tiles(x, x.numel() // (TILE * HEAD_DIM), bits, axis, n_iter=n_iter, stream=stream)
+
+
+def dequantize_tiles(packed: torch.Tensor, n_tiles: int, bits: int, axis: int, out: torch.Tensor, *,
+                     tile_stride: int = TILE * HEAD_DIM, token_stride: int = HEAD_DIM,
+                     src_index: torch.Tensor | None = None, dst_offset: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    st = load().kvarn_dequantize_tiles(_ptr(packed), _ptr(src_index), n_tiles, bits, axis, _ptr(out),
+                                       _DT[out.dtype], tile_stride, token_stride, _ptr(dst_offset), _stream(stream))
+    _check("kvarn_dequantize_tiles", st)
+    return out
+
+
+def dequantize(packed: torch.Tensor, bits: int, axis: int, dtype=torch.float32, stream=None) -> torch.Tensor:
+    """Records [n, Pb] -> tiles [n, 128, 128] of ``dtype``."""
+    n = packed.shape[0]
+    out = torch.empty((n, TILE, HEAD_DIM), dtype=dtype, device=packed.device)
+    return dequantize_tiles(packed, n, bits, axis, out, stream=stream)
+
+
+def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor, n_tiles_per_seq: torch.Tensor,
+                n_kv_heads: int, max_tiles: int, bits_k: int, bits_v: int, *, block_table: torch.Tensor | None = None,
+                sm_scale: float | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q fp16 [batch][n_q_heads][128] -> attention output fp16 of the same shape."""
+    batch, n_q_heads, _ = q.shape
+    if sm_scale is None:
+        sm_scale = HEAD_DIM ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    need = workspace_bytes(batch, n_q_heads, n_kv_heads, max_tiles)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    n_records = min(k_packed.shape[0], v_packed.shape[0])
+    st = load().kvarn_decode_attn(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table), _ptr(n_tiles_per_seq),
+                                  n_records, batch, n_q_heads, n_kv_heads, max_tiles, bits_k, bits_v,
+                                  float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("kvarn_decode_attn", st)
+    return out

@@ -1,0 +1,102 @@
+"""The C ABI library loads on a machine without a GPU, exports every function
+declared in include/kvarn.h, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_quantization_x128_amd import kvarn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p
+A = P(0x10000)          # 16-byte aligned stand-in addresses: validation never dereferences them
+A2 = P(0x20000)
+MIS = P(0x10008)        # 8-byte aligned only
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kvarn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvarn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = kvarn.load()
+    names = header_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(kvarn.SIGNATURES) == names
+
+
+def test_host_helpers():
+    assert kvarn.format_version() == 1
+    assert kvarn.tile_bytes(2) == 4608 and kvarn.tile_bytes(4) == 8704 and kvarn.tile_bytes(3) == 0
+    assert kvarn.parse_preset("kvarn_k4v2_g128") == (4, 2, 128)
+    assert kvarn.parse_preset("kvarn_k2v2_g128") == (2, 2, 128)
+    for bad, st in [("kvarn_k3v2_g128", kvarn.EUNSUPPORTED), ("kvarn_k4v2_g64", kvarn.EUNSUPPORTED),
+                    ("kivi_k2v2", kvarn.EINVAL), ("kvarn_k4v2_g128x", kvarn.EINVAL), ("", kvarn.EINVAL)]:
+        with pytest.raises(kvarn.KvarnError) as e:
+            kvarn.parse_preset(bad)
+        assert e.value.status == st
+    assert kvarn.status_string(kvarn.EALIGN) == "misaligned pointer or stride"
+
+
+def q(x=A, dt=kvarn.BF16, n=1, ts=16384, tok=128, off=None, bits=2, axis=0, it=8, out=A2, dst=None):
+    return kvarn.load().kvarn_quantize_tiles(x, dt, n, ts, tok, off, bits, axis, it, out, dst, None)
+
+
+def test_quantize_argument_errors():
+    assert q(x=None) == kvarn.EINVAL
+    assert q(out=None) == kvarn.EINVAL
+    assert q(dt=7) == kvarn.EINVAL
+    assert q(axis=2) == kvarn.EINVAL
+    assert q(bits=3) == kvarn.EUNSUPPORTED
+    assert q(n=-1) == kvarn.EINVAL
+    assert q(it=-1) == kvarn.EINVAL and q(it=65) == kvarn.EINVAL
+    assert q(tok=64) == kvarn.EINVAL
+    assert q(x=MIS) == kvarn.EALIGN
+    assert q(out=MIS) == kvarn.EALIGN
+    assert q(tok=132) == kvarn.EALIGN
+    assert q(ts=16388) == kvarn.EALIGN
+    assert q(off=P(0x10004)) == kvarn.EALIGN
+    assert q(n=0) == kvarn.OK  # empty batch: a no-op that touches no device
+
+
+def dq(rec=A, src=None, n=1, bits=2, axis=1, out=A2, dt=kvarn.F32, ts=16384, tok=128, off=None):
+    return kvarn.load().kvarn_dequantize_tiles(rec, src, n, bits, axis, out, dt, ts, tok, off, None)
+
+
+def test_dequantize_argument_errors():
+    assert dq(rec=None) == kvarn.EINVAL
+    assert dq(out=None) == kvarn.EINVAL
+    assert dq(dt=3) == kvarn.EINVAL
+    assert dq(bits=8) == kvarn.EUNSUPPORTED
+    assert dq(rec=MIS) == kvarn.EALIGN
+    assert dq(src=P(0x10002)) == kvarn.EALIGN
+    assert dq(tok=100) == kvarn.EINVAL
+    assert dq(n=0) == kvarn.OK
+
+
+def da(qp=A, k=A, v=A, bt=None, nt=A, nrec=10, b=2, hq=8, hkv=2, mt=4, bk=2, bv=2, out=A2, ws=A, wsb=1 << 20):
+    return kvarn.load().kvarn_decode_attn(qp, k, v, bt, nt, nrec, b, hq, hkv, mt, bk, bv, 0.088, out, ws, wsb, None)
+
+
+def test_decode_argument_errors():
+    assert da(qp=None) == kvarn.EINVAL
+    assert da(nt=None) == kvarn.EINVAL
+    assert da(hq=6, hkv=4) == kvarn.EINVAL
+    assert da(hq=32, hkv=2) == kvarn.EUNSUPPORTED  # 16 query heads per KV head
+    assert da(bk=3) == kvarn.EUNSUPPORTED
+    assert da(qp=MIS) == kvarn.EALIGN
+    assert da(ws=None) == kvarn.EWORKSPACE
+    assert da(wsb=16) == kvarn.EWORKSPACE
+    assert da(b=0) == kvarn.OK
+
+
+def test_decode_workspace_plan():
+    # 16 sequences x 8 KV heads x 256 tiles -> 16 splits of 16 tiles
+    assert kvarn.workspace_bytes(16, 32, 8, 256) == 16 * 32 * 16 * 130 * 4
+    assert kvarn.workspace_bytes(1, 4, 1, 3) == 1 * 4 * 3 * 130 * 4
+    assert kvarn.workspace_bytes(2, 4, 1, 0) == 2 * 4 * 1 * 130 * 4

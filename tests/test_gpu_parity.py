@@ -1,0 +1,230 @@
+"""GPU parity of the HIP codec (through the C ABI) against the oracle.
+
+Quantise: the comparison protocol in parity.py (metadata first, codes
+re-derived by the oracle with the GPU's metadata, >= 99.99 % raw identical
+codes, nothing unexplained).  Dequantise: fp32 output within 1e-3 x tile RMS of
+the oracle (observed ~1e-6); 16-bit outputs are the round-to-nearest-even of the
+oracle value.  Inputs are the seeded synthetic workloads of
+kv_cache_quantization_x128_amd.synth; the oracle reads the very bytes the GPU
+consumed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from helpers import tiles_bits
+from kv_cache_quantization_x128_amd import kvarn, synth
+
+pytestmark = pytest.mark.gpu
+K, V = kvarn.AXIS_K, kvarn.AXIS_V
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _gpu_quantize_dense(x_dev, bits, axis, n_iter=8):
+    rec = kvarn.quantize(x_dev, bits, axis, n_iter=n_iter)
+    torch.cuda.synchronize()
+    return rec.cpu().numpy()
+
+
+# ------------------------------------------------------------------------------------- tiny
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("axis", [K, V])
+def test_tiny_quantize_and_dequantize(dev, bits, axis):
+    k, v = synth.tiny()
+    x = k if axis == K else v
+    _log("tiny", bits, axis)
+    gpu = _gpu_quantize_dense(torch.from_numpy(x).to(dev), bits, axis)
+    view = oracle.TileView.dense(tiles_bits(x), oracle.DT_F16)
+    rep = parity.compare_quantize(view, bits, axis, gpu)
+    _log(rep)
+    parity.assert_quantize_parity(rep)
+    # dequantise the GPU's own records: fp32 against the oracle's dequantisation of them
+    out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), bits, axis, torch.float32).cpu().numpy()
+    ref = oracle.dequantize(gpu, bits, axis)
+    assert parity.dequant_fp32_error(out, ref) < 1e-3
+
+
+# ------------------------------------------------------------------------------------- dequant
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_dequantize_oracle_records(dev, bits, axis, dtype):
+    """The GPU dequantises records written by the oracle (no GPU quantiser involved)."""
+    rng = np.random.default_rng(100 + bits + 4 * axis)
+    x = (rng.standard_normal((11, 128, 128)) * np.exp(rng.normal(0, 1, (11, 1, 128)))).astype(np.float16)
+    rec = oracle.quantize(oracle.TileView.dense(tiles_bits(x), oracle.DT_F16), bits, axis)
+    ref = oracle.dequantize(rec, bits, axis)
+    out = kvarn.dequantize(torch.from_numpy(rec).to(dev), bits, axis, dtype)
+    torch.cuda.synchronize()
+    if dtype == torch.float32:
+        err = parity.dequant_fp32_error(out.cpu().numpy(), ref)
+        _log("dequant fp32 max err / tile rms", err)
+        assert err < 1e-3
+    else:
+        ok = parity.rounded_output_ok(out, ref)
+        assert ok.all(), np.argwhere(~ok)[:5]
+
+
+# ------------------------------------------------------------------------------------- edge cases
+def _edge_tiles():
+    rng = np.random.default_rng(7)
+    base = rng.standard_normal((128, 128)).astype(np.float32)
+    tiles = {
+        "zero": np.zeros((128, 128), np.float32),
+        "constant": np.full((128, 128), 0.75, np.float32),
+        "zero_row": base.copy(),
+        "const_channel": base.copy(),
+        "huge": base * 3000.0,
+        "small": base * 0.02,
+        "offset_channels": base + rng.normal(0, 3, (1, 128)).astype(np.float32),
+        "one_spike": np.zeros((128, 128), np.float32),
+        "ints": rng.integers(-3, 4, (128, 128)).astype(np.float32),
+    }
+    tiles["zero_row"][17] = 0
+    tiles["const_channel"][:, 5] = 1.5
+    tiles["one_spike"][40, 99] = 7.0
+    return tiles
+
+
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_edge_case_tiles(dev, axis, bits):
+    tiles = _edge_tiles()
+    names = list(tiles)
+    x = np.stack([tiles[n] for n in names])
+    _log("edge", names)
+    gpu = _gpu_quantize_dense(torch.from_numpy(x).to(dev), bits, axis)
+    rep = parity.compare_quantize(oracle.TileView.dense(x, oracle.DT_F32), bits, axis, gpu)
+    _log(rep)
+    parity.assert_quantize_parity(rep, min_identical=0.999)
+    out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), bits, axis, torch.float32).cpu().numpy()
+    assert parity.dequant_fp32_error(out, oracle.dequantize(gpu, bits, axis)) < 1e-3
+    assert not out[0].any()  # the zero tile comes back exactly zero
+
+
+@pytest.mark.parametrize("n_iter", [0, 1, 3, 20])
+def test_iteration_counts(dev, n_iter):
+    k, _ = synth.tiny(seed=31)
+    gpu = _gpu_quantize_dense(torch.from_numpy(k).to(dev), 2, K, n_iter=n_iter)
+    rep = parity.compare_quantize(oracle.TileView.dense(tiles_bits(k), oracle.DT_F16), 2, K, gpu, n_iter=n_iter)
+    _log(n_iter, rep)
+    parity.assert_quantize_parity(rep)
+
+
+def test_addressing_offsets_index_and_misalignment(dev):
+    """Tile offsets (including ones that are not 8-element aligned), a permuted
+    destination index and strided tokens give the same records as dense tiles."""
+    rng = np.random.default_rng(9)
+    dense = rng.standard_normal((5, 128, 128)).astype(np.float16)
+    ref = _gpu_quantize_dense(torch.from_numpy(dense).to(dev), 2, V)
+    token_stride = 136                                         # padded rows
+    buf = np.zeros(6 * 128 * token_stride + 64, np.float16)
+    offs = np.array([0, 128 * token_stride + 3, 2 * 128 * token_stride + 8,
+                     3 * 128 * token_stride + 5, 4 * 128 * token_stride + 16], np.int64)
+    for i, o in enumerate(offs):
+        for t in range(128):
+            buf[o + t * token_stride: o + t * token_stride + 128] = dense[i, t]
+    perm = np.array([3, 0, 4, 1, 2], np.int64)
+    out = torch.zeros((5, kvarn.tile_bytes(2)), dtype=torch.uint8, device=dev)
+    kvarn.quantize_tiles(torch.from_numpy(buf).to(dev), 5, 2, V, token_stride=token_stride,
+                         tile_offset=torch.from_numpy(offs).to(dev), out=out,
+                         dst_index=torch.from_numpy(perm).to(dev))
+    got = out.cpu().numpy()
+    assert np.array_equal(got[perm], ref)
+    # and back through the same strided layout
+    back = torch.zeros(buf.shape, dtype=torch.float16, device=dev)
+    kvarn.dequantize_tiles(out, 5, 2, V, back, token_stride=token_stride,
+                           src_index=torch.from_numpy(perm).to(dev), dst_offset=torch.from_numpy(offs).to(dev))
+    deq = kvarn.dequantize(torch.from_numpy(ref).to(dev), 2, V, torch.float16).cpu().numpy()
+    b = back.cpu().numpy()
+    for i, o in enumerate(offs):
+        for t in (0, 77, 127):
+            assert np.array_equal(b[o + t * token_stride: o + t * token_stride + 128], deq[i, t])
+
+
+def test_empty_batch_is_noop(dev):
+    x = torch.zeros((1, 128, 128), dtype=torch.bfloat16, device=dev)
+    out = torch.full((1, 4608), 7, dtype=torch.uint8, device=dev)
+    kvarn.quantize_tiles(x, 0, 2, K, out=out)
+    kvarn.dequantize_tiles(out, 0, 2, K, torch.zeros_like(x))
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+
+
+# ------------------------------------------------------------------------------------- full sizes
+def _sample_dense(x_flat, offsets, idx, token_stride):
+    """Gather tiles (exact bytes) at offsets[idx] of a flat 16-bit tensor into [n,128,128]."""
+    o = offsets[idx]
+    t = torch.arange(128, device=x_flat.device)[:, None] * token_stride + torch.arange(128, device=x_flat.device)
+    return x_flat[o[:, None, None] + t[None]]
+
+
+def _check_sample(x_flat, offsets, token_stride, rec, bits, axis, n_sample, seed):
+    n = offsets.numel()
+    idx = torch.from_numpy(np.random.default_rng(seed).choice(n, size=min(n, n_sample), replace=False)).to(
+        offsets.device)
+    tiles = _sample_dense(x_flat, offsets, idx, token_stride)
+    view = oracle.TileView.dense(parity.bits_of(tiles), oracle.DT_BF16)
+    gpu = rec[idx].cpu().numpy()
+    rep = parity.compare_quantize(view, bits, axis, gpu)
+    _log(rep)
+    parity.assert_quantize_parity(rep)
+    # dequantise the sample on the GPU (fp32) against the oracle
+    out = kvarn.dequantize(rec[idx].contiguous(), bits, axis, torch.float32).cpu().numpy()
+    assert parity.dequant_fp32_error(out, oracle.dequantize(gpu, bits, axis)) < 1e-3
+
+
+def test_decode_append_full_size(dev):
+    """36 layers x 64 sequences x 8 KV heads, one new 128-token block each, bf16,
+    token-major [layer][seq][token][head][128]; every tile quantised, 1024 sampled
+    per cache checked against the oracle; a second run is byte-identical."""
+    L_, B_, H_ = 36, 64, 8
+    k, v = synth.decode_append(n_layers=L_, n_seq=B_, n_heads=H_, device=dev)
+    offs = synth.decode_append_offsets(L_, B_, H_, device=dev)
+    n = offs.numel()
+    ts = H_ * 128
+    for name, x, axis in (("K", k, K), ("V", v, V)):
+        _log("decode_append", name, n)
+        rec = kvarn.quantize_tiles(x, n, 2, axis, token_stride=ts, tile_offset=offs)
+        rec2 = kvarn.quantize_tiles(x, n, 2, axis, token_stride=ts, tile_offset=offs)
+        torch.cuda.synchronize()
+        assert torch.equal(rec, rec2)
+        _check_sample(x.view(-1), offs, ts, rec, 2, axis, 1024, seed=5 + axis)
+        # round trip into the same strided layout
+        back = torch.empty_like(x)
+        kvarn.dequantize_tiles(rec, n, 2, axis, back, token_stride=ts, dst_offset=offs)
+        ref16 = kvarn.dequantize(rec[:8].contiguous(), 2, axis, torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(back[0, 0, :, :8].permute(1, 0, 2), ref16)
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def test_prefill_full_size(dev):
+    """36 layers x 8 KV heads x 32768 tokens (bf16): all 147456 tiles, 512 sampled per cache."""
+    k, v = synth.prefill(device=dev)
+    for name, x, axis in (("K", k, K), ("V", v, V)):
+        _log("prefill", name)
+        rec = kvarn.quantize(x, 2, axis)
+        offs = torch.arange(rec.shape[0], device=dev, dtype=torch.int64) * 16384
+        _check_sample(x.view(-1), offs, 128, rec, 2, axis, 512, seed=11 + axis)
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def test_phi4_full_size(dev):
+    """Phi-4-14B shape: 40 layers x 10 KV heads x 8 sequences x 16384 tokens, 4-bit K, 2-bit V."""
+    k, v = synth.phi4(device=dev)
+    for name, x, axis, bits in (("K", k, K, 4), ("V", v, V, 2)):
+        _log("phi4", name)
+        rec = kvarn.quantize(x, bits, axis)
+        offs = torch.arange(rec.shape[0], device=dev, dtype=torch.int64) * 16384
+        _check_sample(x.view(-1), offs, 128, rec, bits, axis, 512, seed=21 + axis)
+        del rec
+    del k, v
+    torch.cuda.empty_cache()
