@@ -617,8 +617,8 @@ int kvo_dequantize_tiles(const uint8_t *records, int64_t n_tiles, int bits, int 
  * h = hq / (n_q_heads / n_kv_heads) (at most 64 query heads per KV head),
  * tile j < min(n_tiles[b], max_tiles) is record
  *   idx = block_table ? block_table[row] : row,  row = (b * n_kv_heads + h) * max_tiles + j
- * of k_rec (K layout, bits_k) and v_rec (V layout, bits_v).  The dequantised
- * K and V tiles are rounded to FP16, then
+ * of k_rec (K layout, bits_k) and v_rec (V layout, bits_v).  With the exact
+ * (binary64) dequantised K and V tiles,
  *   s_t = sm_scale * q . k_t,  p = softmax(s),  out = sum_t p_t v_t.
  * A sequence with no tiles gets a zero output.
  */
@@ -650,7 +650,7 @@ int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_re
             for (int g = 0; g < gs; ++g)
                 for (int d = 0; d < N; ++d)
                     qd[g * N + d] = kvo_f16_decode(q[(b * n_q_heads + (int64_t)kvh * gs + g) * N + d]);
-            /* scores s[g][token] = sm_scale * q_g . fp16(k_token) */
+            /* scores s[g][token] = sm_scale * q_g . k_token */
             for (int j = 0; j < nt; ++j) {
                 int64_t row = (b * n_kv_heads + kvh) * (int64_t)max_tiles + j;
                 int64_t idx = block_table ? block_table[row] : row;
@@ -659,7 +659,7 @@ int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_re
                     for (int g = 0; g < gs; ++g) {
                         double acc = 0.0;
                         for (int d = 0; d < N; ++d)
-                            acc += qd[g * N + d] * kvo_f16_round(kt[t * N + d]);
+                            acc += qd[g * N + d] * kt[t * N + d];
                         s[((size_t)g * nt + j) * N + t] = sm_scale * acc;
                     }
             }
@@ -676,7 +676,7 @@ int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_re
                     l[g] += sg[u];
                 }
             }
-            /* out[g] = sum_token p * fp16(v_token) */
+            /* out[g] = sum_token p * v_token */
             for (int j = 0; j < nt; ++j) {
                 int64_t row = (b * n_kv_heads + kvh) * (int64_t)max_tiles + j;
                 int64_t idx = block_table ? block_table[row] : row;
@@ -685,7 +685,7 @@ int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_re
                     for (int t = 0; t < N; ++t) {
                         double p = s[((size_t)g * nt + j) * N + t];
                         for (int d = 0; d < N; ++d)
-                            o[g * N + d] += p * kvo_f16_round(vt[t * N + d]);
+                            o[g * N + d] += p * vt[t * N + d];
                     }
             }
             for (int g = 0; g < gs; ++g)

@@ -91,8 +91,8 @@ def _cache(orc, n_seq, n_kv, n_tiles, seed, bits_k=2, bits_v=2, f=None):
 
 def _brute(orc, q, kr, vr, n_tiles, hq, hkv, max_tiles, bk, bv, block_table=None):
     """Decode attention from the oracle's own dequantised tiles with scipy's softmax."""
-    kd = orc.dequantize(kr, bk, K).astype(np.float16).astype(np.float64)
-    vd = orc.dequantize(vr, bv, V).astype(np.float16).astype(np.float64)
+    kd = orc.dequantize(kr, bk, K)
+    vd = orc.dequantize(vr, bv, V)
     gs = hq // hkv
     out = np.zeros((q.shape[0], hq, N))
     for b in range(q.shape[0]):
@@ -145,7 +145,7 @@ def test_decode_constant_keys_give_mean_value(orc):
     kr, vr = _cache(orc, 1, 1, 2, seed=11, f=const_k)
     q = np.random.default_rng(12).standard_normal((1, 2, N)).astype(np.float16)
     got = orc.decode_attn(q.view(np.uint16), kr, vr, np.array([2], np.int32), 2, 1, 2, 2, 2)
-    vd = orc.dequantize(vr, 2, V).astype(np.float16).astype(np.float64).reshape(-1, N)
+    vd = orc.dequantize(vr, 2, V).reshape(-1, N)
     assert np.abs(got[0] - vd.mean(0)).max() < 1e-12
 
 
@@ -160,7 +160,7 @@ def test_decode_peaked_query_selects_planted_token(orc):
     q = np.zeros((1, 1, N), np.float16)
     q[0, 0, :8] = 30.0
     got = orc.decode_attn(q.view(np.uint16), kr, vr, np.array([1], np.int32), 1, 1, 1, 2, 2)
-    vd = orc.dequantize(vr, 2, V).astype(np.float16).astype(np.float64)[0]
+    vd = orc.dequantize(vr, 2, V)[0]
     assert np.abs(got[0, 0] - vd[77]).max() < 1e-6 * np.abs(vd[77]).max()
 
 
