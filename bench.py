@@ -145,6 +145,20 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
     }
 
 
+def copy_reference(reps=10, nbytes=1 << 30):
+    """A plain device-to-device copy of known size: the achievable-bandwidth
+    reference, and the calibration of the profiler's FETCH/WRITE counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    t = OpTimer()
+    for _ in range(reps):
+        t(lambda: dst.copy_(src))
+    ms = t.mean_ms()
+    return {"bytes_per_launch": 2 * nbytes, "launch_ms": ms, "GBs": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(target_s=15.0, bits=2):
     """The oracle's quantise + dequantise on a bounded sample of decode-append K tiles."""
     import oracle
@@ -186,6 +200,7 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=36)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true", help="also time a plain 1 GiB device copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the codec has no cross-GPU step); got --gpus {args.gpus}",
@@ -237,6 +252,8 @@ def main():
     }
     if not args.no_decode:
         line["decode_attn"] = bench_decode(args.decode_passes, 2, layers=args.decode_layers)
+    if args.copy_calib:
+        line["copy_reference"] = copy_reference()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -93,43 +93,72 @@ __device__ __forceinline__ void fwht_regs(float (&v)[NV]) {
 }
 
 // ---------------------------------------------------------------- lane reductions
-// Sum / max over the 16 lanes that differ in lane bits 0-3.
+// DPP row operations (within each 16-lane row of a wave64).  The compiler fuses
+// the move into the consuming v_add/v_max/v_min (e.g. v_add_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each half row (xor 7)
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within the row (xor 15)
+
+// All-reduce over the 16 lanes of a row.  Each stage combines a lane with a
+// partner holding the same partial with operands swapped, and + / max / min
+// are commutative, so every lane ends with the bit-identical result.
 __device__ __forceinline__ float sum_lanes16(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
+    v += dpp_mov<kDppXor1>(v);
+    v += dpp_mov<kDppXor2>(v);
+    v += dpp_mov<kDppHalfMirror>(v);
+    v += dpp_mov<kDppMirror>(v);
     return v;
 }
 __device__ __forceinline__ float max_lanes16(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, dpp_mov<kDppXor1>(v));
+    v = fmaxf(v, dpp_mov<kDppXor2>(v));
+    v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_mov<kDppMirror>(v));
     return v;
 }
 __device__ __forceinline__ float min_lanes16(float v) {
-    v = fminf(v, __shfl_xor(v, 1));
-    v = fminf(v, __shfl_xor(v, 2));
-    v = fminf(v, __shfl_xor(v, 4));
-    v = fminf(v, __shfl_xor(v, 8));
+    v = fminf(v, dpp_mov<kDppXor1>(v));
+    v = fminf(v, dpp_mov<kDppXor2>(v));
+    v = fminf(v, dpp_mov<kDppHalfMirror>(v));
+    v = fminf(v, dpp_mov<kDppMirror>(v));
     return v;
+}
+
+// Value of lane (l ^ 16): ds_swizzle SWAP mode within 32-lane halves.
+__device__ __forceinline__ float xor16(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+// v[l] op v[l ^ 32] for every lane via v_permlane32_swap: with both operands v,
+// the two results hold (v[l], v[l^32]) in lane-independent order.
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float min_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fminf(__int_as_float(r[0]), __int_as_float(r[1]));
 }
 // Sum / max / min over the 4 lanes that differ in lane bits 4-5.
 __device__ __forceinline__ float sum_lanes_hi(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    v += xor16(v);
+    return sum_xor32(v);
 }
 __device__ __forceinline__ float max_lanes_hi(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    v = fmaxf(v, xor16(v));
+    return max_xor32(v);
 }
 __device__ __forceinline__ float min_lanes_hi(float v) {
-    v = fminf(v, __shfl_xor(v, 16));
-    v = fminf(v, __shfl_xor(v, 32));
-    return v;
+    v = fminf(v, xor16(v));
+    return min_xor32(v);
 }
 
 // ---------------------------------------------------------------- tile row I/O

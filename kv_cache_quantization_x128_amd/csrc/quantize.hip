@@ -36,35 +36,51 @@ namespace kvarn {
 namespace {
 
 constexpr int kPad = 132;                 // LDS row pitch (floats) of the staged tile
-constexpr float kDegRel = 1.52587890625e-05f;        // 2^-16
-constexpr float kDegAbs = 8.673617379884035e-19f;    // 2^-60
+constexpr float kInvN = 1.0f / 128.0f;
+constexpr float kInvNN = 1.0f / 16384.0f;
+constexpr float kDegRel2 = 2.3283064365386963e-10f;  // (2^-16)^2: degenerate if var <= 2^-32 rms^2
+constexpr float kDegAbs = 8.673617379884035e-19f;    // 2^-60 (std floor)
+constexpr float kDegAbs2 = 7.52316384526264e-37f;    // 2^-120 (variance floor)
+constexpr float kMagic = 8388608.0f;                 // 2^23: x + 2^23 rounds x >= 0 to an integer
 
-__device__ __forceinline__ float guarded_std(float sd, float rms) {
-    if (sd > kDegRel * rms && sd >= kDegAbs) return sd;
-    return rms >= kDegAbs ? rms : 1.0f;
-}
+// Factor for a step whose population variance is var: 1/std, or 1/rms when the
+// std is degenerate (at most 2^-16 rms, or below 2^-60); see guarded().
+__device__ __forceinline__ bool std_ok(float var, float rms2) { return var > kDegRel2 * rms2 && var >= kDegAbs2; }
+__device__ __forceinline__ float fallback_std(float rms) { return rms >= kDegAbs ? rms : 1.0f; }
 
-// Sum of v[a] over the 16 channel groups for each of this thread's 8 tokens,
-// plus one extra scalar.  In-wave over lane bits 4-5, then across the 4 waves
-// through buf[4][136].  One barrier; callers alternate between two buffers.
+// Sum over the 16 channel groups of v[a] (this thread's 8 tokens) and of one
+// extra scalar: lane bits 4-5 in-wave, then the 4 waves through buf[4][136].
+// One barrier; callers alternate two buffers so the next write never races a read.
 __device__ __forceinline__ void token_sum8(float (&v)[8], float& extra, float* buf, int tid) {
     const int w = tid >> 6, lane = tid & 63, tg = tid & 15;
 #pragma unroll
     for (int a = 0; a < 8; ++a) v[a] = sum_lanes_hi(v[a]);
     extra = sum_lanes_hi(extra);
-    if ((lane >> 4) == 0) {
-#pragma unroll
-        for (int a = 0; a < 8; ++a) buf[w * 136 + 8 * tg + a] = v[a];
+    if (lane < 16) {
+        float4* d = reinterpret_cast<float4*>(buf + w * 136 + 8 * tg);
+        d[0] = make_float4(v[0], v[1], v[2], v[3]);
+        d[1] = make_float4(v[4], v[5], v[6], v[7]);
         if (tg == 0) buf[w * 136 + 128] = extra;
     }
     __syncthreads();
+    float4 p[4][2];
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
-        v[a] = (buf[8 * tg + a] + buf[136 + 8 * tg + a]) + (buf[272 + 8 * tg + a] + buf[408 + 8 * tg + a]);
+    for (int ww = 0; ww < 4; ++ww) {
+        p[ww][0] = *reinterpret_cast<const float4*>(buf + ww * 136 + 8 * tg);
+        p[ww][1] = *reinterpret_cast<const float4*>(buf + ww * 136 + 8 * tg + 4);
+    }
+    v[0] = (p[0][0].x + p[1][0].x) + (p[2][0].x + p[3][0].x);
+    v[1] = (p[0][0].y + p[1][0].y) + (p[2][0].y + p[3][0].y);
+    v[2] = (p[0][0].z + p[1][0].z) + (p[2][0].z + p[3][0].z);
+    v[3] = (p[0][0].w + p[1][0].w) + (p[2][0].w + p[3][0].w);
+    v[4] = (p[0][1].x + p[1][1].x) + (p[2][1].x + p[3][1].x);
+    v[5] = (p[0][1].y + p[1][1].y) + (p[2][1].y + p[3][1].y);
+    v[6] = (p[0][1].z + p[1][1].z) + (p[2][1].z + p[3][1].z);
+    v[7] = (p[0][1].w + p[1][1].w) + (p[2][1].w + p[3][1].w);
     extra = (buf[128] + buf[136 + 128]) + (buf[272 + 128] + buf[408 + 128]);
 }
 
-// Same pattern for min and max of 8 per-token values.
+// Min and max over the 16 channel groups of 8 per-token values (buf[4][272]).
 __device__ __forceinline__ void token_minmax8(float (&mn)[8], float (&mx)[8], float* buf, int tid) {
     const int w = tid >> 6, lane = tid & 63, tg = tid & 15;
 #pragma unroll
@@ -72,7 +88,7 @@ __device__ __forceinline__ void token_minmax8(float (&mn)[8], float (&mx)[8], fl
         mn[a] = min_lanes_hi(mn[a]);
         mx[a] = max_lanes_hi(mx[a]);
     }
-    if ((lane >> 4) == 0) {
+    if (lane < 16) {
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
             buf[w * 272 + 8 * tg + a] = mn[a];
@@ -90,9 +106,9 @@ __device__ __forceinline__ void token_minmax8(float (&mn)[8], float (&mx)[8], fl
 
 template <int BITS, int AXIS, int DT>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
-                                                          int64_t token_stride, const int64_t* __restrict__ tile_off,
-                                                          int n_iter, uint8_t* __restrict__ packed,
-                                                          const int64_t* __restrict__ dst_index) {
+                                                       int64_t token_stride, const int64_t* __restrict__ tile_off,
+                                                       int n_iter, uint8_t* __restrict__ packed,
+                                                       const int64_t* __restrict__ dst_index) {
     using R = Rec<BITS>;
     __shared__ __align__(16) float sY[kN * kPad];   // staged tile; later the record image
     __shared__ __align__(16) float sRed[2][1088];   // cross-wave partials (two buffers)
@@ -105,14 +121,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     {
         const int t = tid >> 1, h = tid & 1;
         float v[64];
-        const bool vec = (start & 7) == 0;
-        load64<DT>(x, start + (int64_t)t * token_stride + 64 * h, vec, v);
+        load64<DT>(x, start + (int64_t)t * token_stride + 64 * h, (start & 7) == 0, v);
         fwht_regs<64>(v);
+        // last butterfly (channel bit 6) against the partner lane, fused with the
+        // 1/sqrt(128) scale: lane h=0 keeps s*(a+b), lane h=1 keeps s*(a-b)
+        const float sgn = h ? -kInvSqrtN : kInvSqrtN;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            const float p = __shfl_xor(v[i], 1);
-            v[i] = (h ? (p - v[i]) : (v[i] + p)) * kInvSqrtN;
-        }
+        for (int i = 0; i < 64; ++i) v[i] = fmaf(sgn, v[i], dpp_mov<kDppXor1>(v[i]) * kInvSqrtN);
         float4* dst = reinterpret_cast<float4*>(&sY[t * kPad + 64 * h]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -120,7 +135,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     __syncthreads();
 
     // ---- 2. 8x8 block of the rotated tile ----------------------------------------
-    const int tg = tid & 15, cg = tid >> 4;
+    const int tg = tid & 15, cg = tid >> 4;   // tokens 8tg.., channels 8cg..
     float y[8][8];
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
@@ -131,9 +146,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     }
 
     // ---- 3. dual-axis normalisation ----------------------------------------------
-    // Row sums of squares (per token, all channels) and column sums of squares
-    // (per channel, all tokens) give the RMS of each scaled matrix cheaply.
-    float rowsq[8], colsq[8], w[8], u[8], r[8], c[8];
+    // rowsq[a] = sum_j Y_aj^2 (all channels), colsq[j] = sum_i Y_ij^2 (all tokens):
+    // the mean square of w_i Y_ij is sum_i w_i^2 rowsq_i / 128^2, and likewise for u_j.
+    float rowsq[8], colsq[8], w[8], u[8];
     int buf = 0;
     {
         float unused = 0.0f;
@@ -155,15 +170,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = 1.0f, u[k] = 1.0f, r[k] = 1.0f, c[k] = 1.0f;
+    for (int k = 0; k < 8; ++k) w[k] = 1.0f, u[k] = 1.0f;
+    // variances of the last channel / token step, and their rms^2, for the final factors
+    float var_c[8], var_r[8], rms2_c = 0.0f, rms2_r = 0.0f;
 
-    constexpr float kInvN = 1.0f / 128.0f;
     for (int it = 0; it < n_iter; ++it) {
-        // channel step on A_ij = w_i Y_ij
+        // channel step on A_ij = w_i Y_ij: c_j = std_i A_ij, u_j = 1 / c_j
         float ss = 0.0f;
 #pragma unroll
         for (int a = 0; a < 8; ++a) ss = fmaf(w[a] * w[a], rowsq[a], ss);
-        const float rms_c = sqrtf(sum_lanes16(ss)) * kInvN;
+        rms2_c = sum_lanes16(ss) * kInvNN;
         float mu[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -180,10 +196,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
                 const float d = fmaf(w[a], y[a][j], -mu[j]);
                 s = fmaf(d, d, s);
             }
-            c[j] = guarded_std(sqrtf(sum_lanes16(s) * kInvN), rms_c);
-            u[j] = 1.0f / c[j];
+            var_c[j] = sum_lanes16(s) * kInvN;
         }
-        // token step on B_ij = u_j Y_ij
+        {
+            const float fb = 1.0f / fallback_std(sqrtf(rms2_c));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) u[j] = std_ok(var_c[j], rms2_c) ? __builtin_amdgcn_rsqf(var_c[j]) : fb;
+        }
+        // token step on B_ij = u_j Y_ij: r_i = std_j B_ij, w_i = 1 / r_i
         float m[8], q = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) q = fmaf(u[j] * u[j], colsq[j], q);
@@ -196,8 +216,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         }
         token_sum8(m, q, sRed[buf], tid);
         buf ^= 1;
-        const float rms_r = sqrtf(q) * kInvN;
-        float v2[8], dummy = 0.0f;
+        rms2_r = q * kInvNN;
+        float dummy = 0.0f;
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
             const float mean = m[a] * kInvN;
@@ -207,22 +227,34 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
                 const float d = fmaf(u[j], y[a][j], -mean);
                 s = fmaf(d, d, s);
             }
-            v2[a] = s;
+            var_r[a] = s;
         }
-        token_sum8(v2, dummy, sRed[buf], tid);
+        token_sum8(var_r, dummy, sRed[buf], tid);
         buf ^= 1;
+        {
+            const float fb = 1.0f / fallback_std(sqrtf(rms2_r));
 #pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            r[a] = guarded_std(sqrtf(v2[a] * kInvN), rms_r);
-            w[a] = 1.0f / r[a];
+            for (int a = 0; a < 8; ++a) {
+                var_r[a] *= kInvN;
+                w[a] = std_ok(var_r[a], rms2_r) ? __builtin_amdgcn_rsqf(var_r[a]) : fb;
+            }
         }
     }
 
-    // ---- 4. second scale with a power-of-two gauge, then FP8 ----------------------
-    // g = r (per token) for K, c (per channel) for V.
-    float gsum = 0.0f;
+    // ---- 4. second scale: g = r (K, per token) or c (V, per channel) --------------
+    // g from the last step with a correctly rounded sqrt (1 when no iteration ran),
+    // power-of-two gauge from the exponent of its mean, then FP8 E4M3.
+    float g[8];
+    {
+        const float rms2 = (AXIS == kAxisK) ? rms2_r : rms2_c;
+        const float fb = fallback_std(sqrtf(rms2));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) gsum += (AXIS == kAxisK) ? r[k] : c[k];
+        for (int k = 0; k < 8; ++k) {
+            const float var = (AXIS == kAxisK) ? var_r[k] : var_c[k];
+            g[k] = n_iter == 0 ? 1.0f : (std_ok(var, rms2) ? sqrtf(var) : fb);
+        }
+    }
+    float gsum = ((g[0] + g[1]) + (g[2] + g[3])) + ((g[4] + g[5]) + (g[6] + g[7]));
     if constexpr (AXIS == kAxisK) {
         gsum = sum_lanes16(gsum);                      // over the 16 token groups
     } else {
@@ -230,19 +262,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         token_sum8(dummy8, gsum, sRed[buf], tid);      // over the 16 channel groups
         buf ^= 1;
     }
-    const float gmean = gsum * kInvN;
-    int gexp = (int)((__float_as_uint(gmean) >> 23) & 255u) - 126;  // frexp exponent
+    int gexp = (int)((__float_as_uint(gsum * kInvN) >> 23) & 255u) - 126;  // frexp exponent of the mean
     gexp = gexp < -126 ? -126 : (gexp > 126 ? 126 : gexp);
     const float gscale = pow2f(-gexp);
     uint32_t s2code[8];
     float inv_s2[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const float g = ((AXIS == kAxisK) ? r[k] : c[k]) * gscale;
-        uint32_t code = fp8_encode_nonneg(g);
+        uint32_t code = fp8_encode_nonneg(g[k] * gscale);
         code = code < 1u ? 1u : code;                  // floor 2^-9
         s2code[k] = code;
-        inv_s2[k] = 1.0f / fp8_decode_nonneg(code);
+        inv_s2[k] = __builtin_amdgcn_rcpf(fp8_decode_nonneg(code));
     }
 
     // ---- 5. Zn, group statistics, FP8 s1 / FP16 z ----------------------------------
@@ -256,37 +286,39 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     if constexpr (AXIS == kAxisK) {                    // groups = channels, over tokens
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float lo = y[0][j], hi = y[0][j];
-#pragma unroll
-            for (int a = 1; a < 8; ++a) lo = fminf(lo, y[a][j]), hi = fmaxf(hi, y[a][j]);
+            float lo = fminf(fminf(y[0][j], y[1][j]), fminf(y[2][j], y[3][j]));
+            float hi = fmaxf(fmaxf(y[0][j], y[1][j]), fmaxf(y[2][j], y[3][j]));
+            lo = fminf(lo, fminf(fminf(y[4][j], y[5][j]), fminf(y[6][j], y[7][j])));
+            hi = fmaxf(hi, fmaxf(fmaxf(y[4][j], y[5][j]), fmaxf(y[6][j], y[7][j])));
             gmin[j] = min_lanes16(lo);
             gmax[j] = max_lanes16(hi);
         }
     } else {                                           // groups = tokens, over channels
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
-            float lo = y[a][0], hi = y[a][0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j) lo = fminf(lo, y[a][j]), hi = fmaxf(hi, y[a][j]);
-            gmin[a] = lo;
-            gmax[a] = hi;
+            gmin[a] = fminf(fminf(fminf(y[a][0], y[a][1]), fminf(y[a][2], y[a][3])),
+                            fminf(fminf(y[a][4], y[a][5]), fminf(y[a][6], y[a][7])));
+            gmax[a] = fmaxf(fmaxf(fmaxf(y[a][0], y[a][1]), fmaxf(y[a][2], y[a][3])),
+                            fmaxf(fmaxf(y[a][4], y[a][5]), fmaxf(y[a][6], y[a][7])));
         }
         token_minmax8(gmin, gmax, sRed[buf], tid);
         buf ^= 1;
     }
     uint32_t s1code[8], zbits[8];
-    float inv_s1[8], zval[8];
+    float inv_s1[8], zoff[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        uint32_t code = fp8_encode_nonneg((gmax[k] - gmin[k]) / kL);
+        uint32_t code = fp8_encode_nonneg((gmax[k] - gmin[k]) * (1.0f / kL));
         code = code < 1u ? 1u : code;                  // floor 2^-9
         s1code[k] = code;
-        inv_s1[k] = 1.0f / fp8_decode_nonneg(code);
+        inv_s1[k] = __builtin_amdgcn_rcpf(fp8_decode_nonneg(code));
         zbits[k] = f32_to_f16_bits_sat(gmin[k]);
-        zval[k] = f16_bits_to_f32(zbits[k]);
+        zoff[k] = -f16_bits_to_f32(zbits[k]) * inv_s1[k];
     }
 
     // ---- 6. codes into the LDS record image, then 16-byte stores --------------------
+    // t = (Zn - z) / s1, clamped to [0, L]; adding 2^23 rounds it to the nearest
+    // integer (ties to even) in the low mantissa bits.
     __syncthreads();                                   // everyone is done with sY as floats
     uint8_t* img = reinterpret_cast<uint8_t*>(sY);
 #pragma unroll
@@ -295,9 +327,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int gi = (AXIS == kAxisK) ? j : a;
-            const float t = (y[a][j] - zval[gi]) * inv_s1[gi];
-            const float qc = fminf(fmaxf(__builtin_rintf(t), 0.0f), kL);
-            word |= (uint32_t)qc << (BITS * j);
+            float t = fmaf(y[a][j], inv_s1[gi], zoff[gi]);
+            t = __builtin_amdgcn_fmed3f(t, 0.0f, kL) + kMagic;
+            word |= (__float_as_uint(t) - 0x4B000000u) << (BITS * j);
         }
         const int tok = 8 * tg + a;
         if constexpr (BITS == 2)

@@ -1,0 +1,63 @@
+"""The comparison protocol accepts the oracle's own records and flags planted
+mistakes: it must not excuse real errors as rounding."""
+import numpy as np
+import pytest
+
+import oracle
+import parity
+from helpers import tiles_bits
+from kv_cache_quantization_x128_amd import synth
+
+
+@pytest.fixture(scope="module")
+def case():
+    k, v = synth.tiny()
+    view = oracle.TileView.dense(tiles_bits(k)[:3], oracle.DT_F16)
+    rec = oracle.quantize(view, 2, 0)
+    return view, rec
+
+
+def test_own_records_pass(case):
+    view, rec = case
+    rep = parity.compare_quantize(view, 2, 0, rec)
+    assert rep["unexplained"] == 0 and rep["raw_identical_codes"] == 1.0
+
+
+def _corrupt(rec, fn):
+    r = rec.copy()
+    fn(r)
+    return r
+
+
+@pytest.mark.parametrize("name", ["code_plus2", "code_plus1_far_from_tie", "s2_two_steps", "z_far", "s1_swap"])
+def test_planted_mistakes_are_flagged(case, name):
+    view, rec = case
+    c = 2048 * 2
+
+    def code_plus2(r):             # token 3, channel 0 code += 2 (mod 4)
+        b = r[1, 3 * 32]
+        r[1, 3 * 32] = (int(b) & 0xFC) | (((int(b) & 0x3) + 2) & 0x3)
+
+    def code_plus1_far_from_tie(r):
+        codes, t = oracle.codes_given_meta(view, 2, 0, rec)
+        frac = np.abs(np.abs(t[0] - np.floor(t[0])) - 0.5)
+        i, j = np.unravel_index(np.argmax(frac * (codes[0] < 3)), frac.shape)  # most decisive code below 3
+        byte = i * 32 + (j * 2) // 8
+        sh = (j * 2) % 8
+        cur = (r[0, byte] >> sh) & 3
+        r[0, byte] = (int(r[0, byte]) & (0xFF ^ (3 << sh))) | ((int(cur) + 1) << sh)
+
+    def s2_two_steps(r):
+        r[2, c + 128 + 10] += 2
+
+    def z_far(r):
+        z = r[0, c + 256: c + 512].view(np.float16).copy()
+        z[5] = np.float16(float(z[5]) + 1.0)
+        r[0, c + 256: c + 512] = z.view(np.uint8)
+
+    def s1_swap(r):
+        r[1, c + 7], r[1, c + 90] = r[1, c + 90], r[1, c + 7] + 3
+
+    bad = _corrupt(rec, locals()[name])
+    rep = parity.compare_quantize(view, 2, 0, bad)
+    assert rep["unexplained"] > 0, (name, str(rep))
