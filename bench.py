@@ -31,10 +31,35 @@ from kv_cache_quantization_x128_amd import kvarn, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 TILE_F16_BYTES = 128 * 128 * 2
+CSRC = os.path.join(ROOT, "kv_cache_quantization_x128_amd", "csrc")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic_decode_append.json")
+KERNEL_SOURCES = {"quantize": ("quantize.hip", "kvarn_device.h"), "dequantize": ("dequantize.hip", "kvarn_device.h"),
+                  "decode_partial": ("decode_attn.hip", "kvarn_device.h")}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+    (scaled by the copy-kernel calibration), or None when the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    import json as _json
+
+    try:
+        rec = _json.load(open(TRAFFIC))
+        k = rec["kernels"][kernel]
+        cal = rec["calibration"]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    if h.hexdigest()[:16] != k["source_sha256_16"]:
+        return None
+    return 1024 * (k["fetch_kib"] * cal["fetch_scale"] + k["write_kib"] * cal["write_scale"])
 
 
 class OpTimer:
@@ -140,23 +165,25 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
         "wall_s_per_pass": wall / passes,
         "fp16_equiv_GBs": 2 * batch * hkv * nt * TILE_F16_BYTES / (layer_ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": alg_bytes},
+                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode_partial"),
+                     "algorithmic_bytes_per_launch": alg_bytes},
         "tokens_per_s": batch * hq / (layer_ms * 1e-3),
     }
 
 
-def copy_reference(reps=10, nbytes=1 << 30):
-    """A plain device-to-device copy of known size: the achievable-bandwidth
-    reference, and the calibration of the profiler's FETCH/WRITE counters."""
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+def copy_reference(reps=10, nbytes=1 << 28):
+    """A plain elementwise copy (one dispatch, fp32, read nbytes + write nbytes): the
+    achievable-bandwidth reference, and the calibration of the profiler's
+    FETCH/WRITE counters."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
-    src.fill_(1)
-    dst.copy_(src)
+    torch.mul(src, 1.0, out=dst)
     t = OpTimer()
     for _ in range(reps):
-        t(lambda: dst.copy_(src))
+        t(lambda: torch.mul(src, 1.0, out=dst))
     ms = t.mean_ms()
-    return {"bytes_per_launch": 2 * nbytes, "launch_ms": ms, "GBs": 2 * nbytes / (ms * 1e-3) / 1e9}
+    return {"kernel": "torch elementwise mul-by-1 copy", "bytes_per_launch": 2 * nbytes, "launch_ms": ms,
+            "GBs": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
 def cpu_baseline(target_s=15.0, bits=2):
@@ -200,7 +227,7 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=36)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calib", action="store_true", help="also time a plain 1 GiB device copy")
+    ap.add_argument("--copy-calib", action="store_true", help="also time a plain 256 MiB device copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the codec has no cross-GPU step); got --gpus {args.gpus}",
@@ -227,7 +254,8 @@ def main():
                      "fp16_equiv_GBs": n * TILE_F16_BYTES / (q_ms * 1e-3) / 1e9},
         "dequantize": {"launch_ms": dq_ms, "tiles_per_launch": n, "tiles_per_s": n / (dq_ms * 1e-3),
                        "algorithmic_GBs": dq_ach, "frac_hbm": dq_ach / HBM_PEAK_GBS,
-                       "fp16_equiv_GBs": n * TILE_F16_BYTES / (dq_ms * 1e-3) / 1e9},
+                       "fp16_equiv_GBs": n * TILE_F16_BYTES / (dq_ms * 1e-3) / 1e9,
+                       "traffic": measured_traffic("dequantize")},
     }
     line = {
         "metric": "KV quantize+dequant GB/s (fp16-equiv) and % of HBM peak on 1 MI355X",
@@ -247,7 +275,8 @@ def main():
                    "tiles_per_step": 2 * n, "layout": "[layer][seq][token][head][128]", "n_iter": 8},
         "frac_of_hbm_peak": value / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": q_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": q_ach / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": q_alg},
+                     "frac": q_ach / HBM_PEAK_GBS, "traffic": measured_traffic("quantize"),
+                     "algorithmic_bytes_per_launch": q_alg},
         "ops": ops,
     }
     if not args.no_decode:
