@@ -19,8 +19,10 @@ LIB = os.path.join(PKG, "libkvarn.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
+# -fno-honor-nans: inputs are finite by contract (include/kvarn.h), so min / max
+# need no NaN canonicalisation and fold their DPP source moves.
 HIPCC_FLAGS = [
-    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]

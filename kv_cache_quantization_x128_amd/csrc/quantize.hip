@@ -1,326 +1,540 @@
 // quantize.hip -- KVarN tile quantiser for gfx950.
 //
 // One 256-thread workgroup (4 waves of 64) turns one 128-token x 128-channel
-// tile into one packed record:
+// tile into one packed record, with the whole tile resident in registers:
+// wave w owns tokens 32w..32w+31; lane l = (rg = l/16, cg = l%16) owns the
+// 8 x 8 block of tokens 32w + 8rg + a (a = 0..7) and channels 8cg + j.
 //
-//   1. load + rotate  thread = (token t = tid/2, channel half h = tid%2) holds
-//                     64 channels; six butterfly stages run in registers, the
-//                     seventh (channel bit 6) against the partner lane, then
-//                     the 1/sqrt(128) scale.  Normalised Walsh-Hadamard
-//                     rotation over head_dim (paperlayer.ai summary of arXiv
-//                     2606.03458v1, section 2 Preliminaries and appendix A).
-//   2. transpose      through LDS into 8x8 blocks: thread = (token group
-//                     tg = tid%16, channel group cg = tid/16); lanes 0-15 of a
-//                     wave share a channel group, so every per-channel sum
-//                     over tokens is an in-wave lane reduction.
-//   3. normalise      n_iter rounds of the dual-axis std normalisation
+//   1. load + rotate  Normalised Walsh-Hadamard rotation over head_dim
+//                     (paperlayer.ai summary of arXiv 2606.03458v1, section 2
+//                     Preliminaries and appendix A).  Three butterfly stages
+//                     run in-lane over the 8 channels; the four stages over the
+//                     16 channel groups run across the 16 lanes of a DPP row,
+//                     each as one v_fmac with a DPP source (quad_perm xor 1,
+//                     quad_perm xor 2, row_ror 8, row_half_mirror).  That
+//                     network computes the 16-point Hadamard transform with its
+//                     outputs permuted (lane cg ends with output group
+//                     out_group(cg)) and every lane's values multiplied by a
+//                     known sign (kWhtSigma); the sign is folded into the
+//                     per-column factors below and never costs an instruction.
+//                     The 1/sqrt(128) is not applied to the values: in the
+//                     alternating normalisation a uniform scale of Y only
+//                     scales the channel factors c, so it is folded into the
+//                     channel-step thresholds and into the final multipliers.
+//   2. normalise      n_iter rounds of the dual-axis std normalisation
 //                     (dimensionstp review 3-2(3); paperlayer.ai summary,
 //                     sections 3 Methods, 4 Experiments and appendix H):
-//                       channel step c_j = std_i(Y_ij / r_i)  (in-wave sums)
-//                       token step   r_i = std_j(Y_ij / c_j)  (LDS across waves)
-//                     each std centred, two-pass, population; a std at most
-//                     2^-16 x the RMS of the matrix being normalised is
-//                     replaced by that RMS.
-//   4. metadata       second scale s2 (K: r per token, V: c per channel) with
-//                     a power-of-two gauge and FP8 rounding; Zn = Y / s2; per
+//                       channel step c_j = std_i(Y_ij / r_i)
+//                       token step   r_i = std_j(Y_ij / c_j)
+//                     Y and Y^2 stay in registers, so each step is two FMAs per
+//                     element (sum and sum of squares; population moments).
+//                     Channel sums are reduce-scattered over lane bits 4-5 with
+//                     v_permlane32_swap / v_permlane16_swap, then summed over
+//                     the 4 waves through LDS (one barrier per round); token
+//                     sums are reduce-scattered within the DPP row.  A column
+//                     or row whose mean is large against its std (mean^2 > 16
+//                     var, where the one-pass moment loses digits) makes the
+//                     step fall back to an exact centred second pass.  A std
+//                     at most 2^-16 x the RMS of the matrix normalised in that
+//                     step is replaced by that RMS.
+//   3. metadata       second scale s2 (K: r per token, V: c per channel) with a
+//                     power-of-two gauge and FP8 rounding; Zn = Y / s2; per
 //                     group min/max -> FP8 s1 = (max - min) / L, FP16 z = min
 //                     (paperlayer.ai summary, appendices D and I; agihunt.info
 //                     note: the group-axis factor is absorbed into the group
-//                     scale).
-//   5. RTN + pack     code = clamp(rint((Zn - z) / s1), 0, L), staged in LDS as
-//                     the record image and written with 16-byte stores.
+//                     scale).  For V the last token step is skipped: its result
+//                     is absorbed into s1 and never stored.
+//   4. RTN + pack     code = clamp(rint((Zn - z) / s1), 0, L); each lane packs
+//                     its 8 codes of a token into 16 (2-bit) or 32 (4-bit) bits
+//                     and stores them straight into the record.
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
 
 namespace kvarn {
 namespace {
 
-constexpr int kPad = 132;                 // LDS row pitch (floats) of the staged tile
 constexpr float kInvN = 1.0f / 128.0f;
 constexpr float kInvNN = 1.0f / 16384.0f;
 constexpr float kDegRel2 = 2.3283064365386963e-10f;  // (2^-16)^2: degenerate if var <= 2^-32 rms^2
-constexpr float kDegAbs = 8.673617379884035e-19f;    // 2^-60 (std floor)
-constexpr float kDegAbs2 = 7.52316384526264e-37f;    // 2^-120 (variance floor)
+constexpr float kDegAbs2 = 7.52316384526264e-37f;    // 2^-120
+constexpr float kCancel = 16.0f;                     // mean^2 > 16 var: exact second pass
 constexpr float kMagic = 8388608.0f;                 // 2^23: x + 2^23 rounds x >= 0 to an integer
 
-// Factor for a step whose population variance is var: 1/std, or 1/rms when the
-// std is degenerate (at most 2^-16 rms, or below 2^-60); see guarded().
-__device__ __forceinline__ bool std_ok(float var, float rms2) { return var > kDegRel2 * rms2 && var >= kDegAbs2; }
-__device__ __forceinline__ float fallback_std(float rms) { return rms >= kDegAbs ? rms : 1.0f; }
+// ---- DPP Hadamard network over the 16 lanes of a row -------------------------
+// Stage k computes v + s_k * v[partner] (s_k = -1 where bit l of kWhtS<k> is set).
+// The four stages realise P * H16 * D: lane cg receives output group
+// out_group(cg) times the sign (-1 where bit cg of kWhtSigma is set); D (input
+// signs) is absorbed by the stage signs.  Derived by tracking the sign of every
+// lane through the butterflies (x_lo + x_hi in the lower lane, x_hi - x_lo in
+// the upper one).
+constexpr uint32_t kWhtS1 = 0x5a5a, kWhtS2 = 0x3c3c, kWhtS3 = 0xff00, kWhtS4 = 0x9696, kWhtSigma = 0x09f6;
+constexpr int kDppRor8 = 0x128;
+__device__ __forceinline__ int out_group(int cg) { return (cg & 4) ? (cg ^ 3) : cg; }
+__device__ __forceinline__ float mask_sign(uint32_t mask, int cg) { return ((mask >> cg) & 1u) ? -1.0f : 1.0f; }
 
-// Sum over the 16 channel groups of v[a] (this thread's 8 tokens) and of one
-// extra scalar: lane bits 4-5 in-wave, then the 4 waves through buf[4][136].
-// One barrier; callers alternate two buffers so the next write never races a read.
-__device__ __forceinline__ void token_sum8(float (&v)[8], float& extra, float* buf, int tid) {
-    const int w = tid >> 6, lane = tid & 63, tg = tid & 15;
-#pragma unroll
-    for (int a = 0; a < 8; ++a) v[a] = sum_lanes_hi(v[a]);
-    extra = sum_lanes_hi(extra);
-    if (lane < 16) {
-        float4* d = reinterpret_cast<float4*>(buf + w * 136 + 8 * tg);
-        d[0] = make_float4(v[0], v[1], v[2], v[3]);
-        d[1] = make_float4(v[4], v[5], v[6], v[7]);
-        if (tg == 0) buf[w * 136 + 128] = extra;
-    }
-    __syncthreads();
-    float4 p[4][2];
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-        p[ww][0] = *reinterpret_cast<const float4*>(buf + ww * 136 + 8 * tg);
-        p[ww][1] = *reinterpret_cast<const float4*>(buf + ww * 136 + 8 * tg + 4);
-    }
-    v[0] = (p[0][0].x + p[1][0].x) + (p[2][0].x + p[3][0].x);
-    v[1] = (p[0][0].y + p[1][0].y) + (p[2][0].y + p[3][0].y);
-    v[2] = (p[0][0].z + p[1][0].z) + (p[2][0].z + p[3][0].z);
-    v[3] = (p[0][0].w + p[1][0].w) + (p[2][0].w + p[3][0].w);
-    v[4] = (p[0][1].x + p[1][1].x) + (p[2][1].x + p[3][1].x);
-    v[5] = (p[0][1].y + p[1][1].y) + (p[2][1].y + p[3][1].y);
-    v[6] = (p[0][1].z + p[1][1].z) + (p[2][1].z + p[3][1].z);
-    v[7] = (p[0][1].w + p[1][1].w) + (p[2][1].w + p[3][1].w);
-    extra = (buf[128] + buf[136 + 128]) + (buf[272 + 128] + buf[408 + 128]);
+// v[lane ^ pattern] within the DPP row (every source lane is valid for these
+// patterns); the compiler folds the move into the consuming add / min / max.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// Min and max over the 16 channel groups of 8 per-token values (buf[4][272]).
-__device__ __forceinline__ void token_minmax8(float (&mn)[8], float (&mx)[8], float* buf, int tid) {
-    const int w = tid >> 6, lane = tid & 63, tg = tid & 15;
+// v[i] += s * v[i] of the DPP partner lane, for 8 registers, as one v_fmac_f32
+// with a DPP source each (the compiler does not fold a DPP move into v_fmac).
+// The leading s_nop covers the wait states a DPP read needs after a VALU write
+// of its source; inside the block every instruction reads a register no
+// earlier instruction of the block wrote.
+#define KVARN_FMAC_DPP8(v, s, CTRL)                                                                  \
+    asm("s_nop 4\n\t"                                                                              \
+        "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+        "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+        "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+        "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+        "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+        "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+        "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+        "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                              \
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]) \
+        : "v"(s))
+
+// ---- swap-based pair reductions across lane bit 5 (32) and bit 4 (16) ----------
+// After permlane32_swap(a, b): a = [a_lo | b_lo], b = [a_hi | b_hi]; a op b leaves
+// the reduced a in lanes 0-31 and the reduced b in lanes 32-63.
+struct OpSum { __device__ static float f(float a, float b) { return a + b; } };
+struct OpMin { __device__ static float f(float a, float b) { return fminf(a, b); } };
+struct OpMax { __device__ static float f(float a, float b) { return fmaxf(a, b); } };
+
+template <class OP>
+__device__ __forceinline__ float rs32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return OP::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// After permlane16_swap(a, b): rows (0,1,2,3) of a = (a0, b0, a2, b2), of b = (a1, b1, a3, b3).
+template <class OP>
+__device__ __forceinline__ float rs16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return OP::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Reduce 16 per-lane values v[2j + k] (column j = 0..7, kind k = 0/1) over lane
+// bits 5 and 4.  Lane (h = bit 5, l = bit 4) returns z[0..3] = kinds 0, 1 of
+// local column 4h + 2l and kinds 0, 1 of column 4h + 2l + 1.  Kind 0 uses OP0,
+// kind 1 uses OP1.
+template <class OP0, class OP1>
+__device__ __forceinline__ void col_rs(const float (&v)[16], float (&z)[4]) {
+    float u[8];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        mn[a] = min_lanes_hi(mn[a]);
-        mx[a] = max_lanes_hi(mx[a]);
+    for (int m = 0; m < 8; ++m) u[m] = (m & 1) ? rs32<OP1>(v[m], v[m + 8]) : rs32<OP0>(v[m], v[m + 8]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) z[m] = (m & 1) ? rs16<OP1>(u[m], u[m + 4]) : rs16<OP0>(u[m], u[m + 4]);
+}
+
+// Reduce 16 per-lane values v[2a + k] (row a = 0..7, kind k) over the 16 lanes
+// of a DPP row.  Lane cg returns kinds 0 and 1 of row 4*b3 + 2*b2 + b1 (b_i = bit
+// i of cg) in z[0], z[1]; lanes cg and cg^1 hold the same result.  Each split
+// stage keeps one half of the values per lane and adds the partner's copy of
+// that half (the partner keeps the other half).
+template <class OP0, class OP1>
+__device__ __forceinline__ void row_rs(const float (&v)[16], int cg, float (&z)[2]) {
+    const bool b3 = cg & 8, b2 = cg & 4, b1 = cg & 2;
+    float u[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float keep = b3 ? v[m + 8] : v[m], give = b3 ? v[m] : v[m + 8];
+        const float p = dpp<kDppRor8>(give);
+        u[m] = (m & 1) ? OP1::f(keep, p) : OP0::f(keep, p);
     }
-    if (lane < 16) {
+    float w4[4];
 #pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            buf[w * 272 + 8 * tg + a] = mn[a];
-            buf[w * 272 + 136 + 8 * tg + a] = mx[a];
+    for (int m = 0; m < 4; ++m) {
+        const float keep = b2 ? u[m + 4] : u[m], give = b2 ? u[m] : u[m + 4];
+        const float p = dpp<kDppHalfMirror>(give);
+        w4[m] = (m & 1) ? OP1::f(keep, p) : OP0::f(keep, p);
+    }
+    float x2[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const float keep = b1 ? w4[m + 2] : w4[m], give = b1 ? w4[m] : w4[m + 2];
+        const float p = dpp<kDppXor2>(give);
+        x2[m] = (m & 1) ? OP1::f(keep, p) : OP0::f(keep, p);
+    }
+    z[0] = OP0::f(x2[0], dpp<kDppXor1>(x2[0]));
+    z[1] = OP1::f(x2[1], dpp<kDppXor1>(x2[1]));
+}
+
+// Sum over all 64 lanes of a wave (every lane gets the same value).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    v = rs16<OpSum>(v, v);
+    return rs32<OpSum>(v, v);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// 1/std factor of one step from the population moments, with the degenerate
+// rule: var <= 2^-32 rms^2 or var < floor2 -> fallback factor fb.
+__device__ __forceinline__ float step_factor(float var, float thr, float floor2, float fb) {
+    return (var > thr && var >= floor2) ? __builtin_amdgcn_rsqf(var) : fb;
+}
+
+// LDS scratch of one workgroup.
+struct Smem {
+    float4 xch[2][4][64];   // cross-wave partials, double-buffered
+    float4 col[4][16][4];   // per wave: (f, f^2) of the 8 columns of each channel group
+    float4 row[4][4][4];    // per wave: (f, f^2) of the 8 rows of each row group
+    float gsum[4];          // per wave: gauge partial sums
+};
+
+template <int DT>
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, bool vec, float (&v)[8]) {
+    if constexpr (DT == kF32) {
+        const float* p = reinterpret_cast<const float*>(x) + e0;
+        if (vec) {
+            const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+            v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = p[i];
+        }
+    } else {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + e0;
+        uint32_t w[4];
+        if (vec) {
+            const uint4 q = *reinterpret_cast<const uint4*>(p);
+            w[0] = q.x, w[1] = q.y, w[2] = q.z, w[3] = q.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = (uint32_t)p[2 * k] | ((uint32_t)p[2 * k + 1] << 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (DT == kBF16) {
+                v[2 * k] = __uint_as_float(w[k] << 16);
+                v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+            } else {
+                v[2 * k] = f16_bits_to_f32(w[k] & 0xFFFFu);
+                v[2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
+            }
         }
     }
+}
+
+// Sum of the four waves' partials in xch[buf][*][lane], fixed order (so every
+// wave holds bit-identical totals).
+template <class OP0, class OP1>
+__device__ __forceinline__ void cross_wave(Smem& sm, int buf, int w, int lane, const float (&z)[4], float (&t)[4]) {
+    sm.xch[buf][w][lane] = make_float4(z[0], z[1], z[2], z[3]);
     __syncthreads();
+    const float4 p0 = sm.xch[buf][0][lane], p1 = sm.xch[buf][1][lane];
+    const float4 p2 = sm.xch[buf][2][lane], p3 = sm.xch[buf][3][lane];
+    t[0] = OP0::f(OP0::f(p0.x, p1.x), OP0::f(p2.x, p3.x));
+    t[1] = OP1::f(OP1::f(p0.y, p1.y), OP1::f(p2.y, p3.y));
+    t[2] = OP0::f(OP0::f(p0.z, p1.z), OP0::f(p2.z, p3.z));
+    t[3] = OP1::f(OP1::f(p0.w, p1.w), OP1::f(p2.w, p3.w));
+}
+
+// Per-lane column values for the lane's 8 columns, published by the owners
+// (lane (h, l) owns local columns 4h + 2l and 4h + 2l + 1) through the wave's LDS.
+__device__ __forceinline__ void col_bcast(Smem& sm, int w, int cg, int hl, float4 mine, float (&f)[8], float (&f2)[8]) {
+    sm.col[w][cg][hl] = mine;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        mn[a] = fminf(fminf(buf[8 * tg + a], buf[272 + 8 * tg + a]), fminf(buf[544 + 8 * tg + a], buf[816 + 8 * tg + a]));
-        mx[a] = fmaxf(fmaxf(buf[136 + 8 * tg + a], buf[408 + 8 * tg + a]),
-                      fmaxf(buf[680 + 8 * tg + a], buf[952 + 8 * tg + a]));
+    for (int k = 0; k < 4; ++k) {
+        const float4 q = sm.col[w][cg][k];
+        f[2 * k] = q.x, f2[2 * k] = q.y, f[2 * k + 1] = q.z, f2[2 * k + 1] = q.w;
     }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Per-lane row values for the lane's 8 rows, published by the row owners (lane
+// cg owns row a = 4 b3 + 2 b2 + b1; lanes cg and cg^1 write the same value).
+__device__ __forceinline__ void row_bcast(Smem& sm, int w, int rg, int a_own, float x, float x2, float (&f)[8],
+                                          float (&f2)[8]) {
+    reinterpret_cast<float2*>(&sm.row[w][rg][0])[a_own] = make_float2(x, x2);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float4 q = sm.row[w][rg][k];
+        f[2 * k] = q.x, f2[2 * k] = q.y, f[2 * k + 1] = q.z, f2[2 * k + 1] = q.w;
+    }
+    __builtin_amdgcn_wave_barrier();
 }
 
 template <int BITS, int AXIS, int DT>
-__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
-                                                       int64_t token_stride, const int64_t* __restrict__ tile_off,
-                                                       int n_iter, uint8_t* __restrict__ packed,
-                                                       const int64_t* __restrict__ dst_index) {
+__global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
+                                                          int64_t token_stride, const int64_t* __restrict__ tile_off,
+                                                          int n_iter, uint8_t* __restrict__ packed,
+                                                          const int64_t* __restrict__ dst_index) {
     using R = Rec<BITS>;
-    __shared__ __align__(16) float sY[kN * kPad];   // staged tile; later the record image
-    __shared__ __align__(16) float sRed[2][1088];   // cross-wave partials (two buffers)
+    __shared__ Smem sm;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int rg = lane >> 4, cg = lane & 15, hl = lane >> 4;  // hl = (bit 5, bit 4) = rg
+    const int og = out_group(cg);                                // output channel group of this lane
+    const float sig = mask_sign(kWhtSigma, cg);                  // sign of this lane's rotated values
+    const int row0 = 32 * w + 8 * rg;                            // first token of this lane's block
+    const int a_own = 4 * ((cg >> 3) & 1) + 2 * ((cg >> 2) & 1) + ((cg >> 1) & 1);  // row owned after row_rs
+    const int jc0 = 2 * hl;                                      // first local column owned after col_rs
     const int64_t tile = blockIdx.x;
     const int64_t start = tile_off ? tile_off[tile] : tile * tile_stride;
 
-    // ---- 1. load half a token row and rotate it --------------------------------
-    {
-        const int t = tid >> 1, h = tid & 1;
-        float v[64];
-        load64<DT>(x, start + (int64_t)t * token_stride + 64 * h, (start & 7) == 0, v);
-        fwht_regs<64>(v);
-        // last butterfly (channel bit 6) against the partner lane, fused with the
-        // 1/sqrt(128) scale: lane h=0 keeps s*(a+b), lane h=1 keeps s*(a-b)
-        const float sgn = h ? -kInvSqrtN : kInvSqrtN;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) v[i] = fmaf(sgn, v[i], dpp_mov<kDppXor1>(v[i]) * kInvSqrtN);
-        float4* dst = reinterpret_cast<float4*>(&sY[t * kPad + 64 * h]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-    }
-    __syncthreads();
-
-    // ---- 2. 8x8 block of the rotated tile ----------------------------------------
-    const int tg = tid & 15, cg = tid >> 4;   // tokens 8tg.., channels 8cg..
+    // ---- 1. load and rotate ------------------------------------------------------
     float y[8][8];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        const float4 lo = *reinterpret_cast<const float4*>(&sY[(8 * tg + a) * kPad + 8 * cg]);
-        const float4 hi = *reinterpret_cast<const float4*>(&sY[(8 * tg + a) * kPad + 8 * cg + 4]);
-        y[a][0] = lo.x, y[a][1] = lo.y, y[a][2] = lo.z, y[a][3] = lo.w;
-        y[a][4] = hi.x, y[a][5] = hi.y, y[a][6] = hi.z, y[a][7] = hi.w;
-    }
-
-    // ---- 3. dual-axis normalisation ----------------------------------------------
-    // rowsq[a] = sum_j Y_aj^2 (all channels), colsq[j] = sum_i Y_ij^2 (all tokens):
-    // the mean square of w_i Y_ij is sum_i w_i^2 rowsq_i / 128^2, and likewise for u_j.
-    float rowsq[8], colsq[8], w[8], u[8];
-    int buf = 0;
     {
-        float unused = 0.0f;
+        const bool vec = ((start | token_stride) & 7) == 0;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) load8<DT>(x, start + (int64_t)(row0 + a) * token_stride + 8 * cg, vec, y[a]);
+        const float s1 = mask_sign(kWhtS1, cg), s2 = mask_sign(kWhtS2, cg);
+        const float s3 = mask_sign(kWhtS3, cg), s4 = mask_sign(kWhtS4, cg);
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
-            float s = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s = fmaf(y[a][j], y[a][j], s);
-            rowsq[a] = s;
+            fwht_regs<8>(y[a]);
         }
-        token_sum8(rowsq, unused, sRed[buf], tid);
-        buf ^= 1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float s = 0.0f;
+        for (int a = 0; a < 8; ++a) KVARN_FMAC_DPP8(y[a], s1, "quad_perm:[1,0,3,2]");
 #pragma unroll
-            for (int a = 0; a < 8; ++a) s = fmaf(y[a][j], y[a][j], s);
-            colsq[j] = sum_lanes16(s);
-        }
+        for (int a = 0; a < 8; ++a) KVARN_FMAC_DPP8(y[a], s2, "quad_perm:[2,3,0,1]");
+#pragma unroll
+        for (int a = 0; a < 8; ++a) KVARN_FMAC_DPP8(y[a], s3, "row_ror:8");
+#pragma unroll
+        for (int a = 0; a < 8; ++a) KVARN_FMAC_DPP8(y[a], s4, "row_half_mirror");
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = 1.0f, u[k] = 1.0f;
-    // variances of the last channel / token step, and their rms^2, for the final factors
-    float var_c[8], var_r[8], rms2_c = 0.0f, rms2_r = 0.0f;
-
-    for (int it = 0; it < n_iter; ++it) {
-        // channel step on A_ij = w_i Y_ij: c_j = std_i A_ij, u_j = 1 / c_j
-        float ss = 0.0f;
-#pragma unroll
-        for (int a = 0; a < 8; ++a) ss = fmaf(w[a] * w[a], rowsq[a], ss);
-        rms2_c = sum_lanes16(ss) * kInvNN;
-        float mu[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float s = 0.0f;
-#pragma unroll
-            for (int a = 0; a < 8; ++a) s = fmaf(w[a], y[a][j], s);
-            mu[j] = sum_lanes16(s) * kInvN;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float s = 0.0f;
-#pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                const float d = fmaf(w[a], y[a][j], -mu[j]);
-                s = fmaf(d, d, s);
-            }
-            var_c[j] = sum_lanes16(s) * kInvN;
-        }
-        {
-            const float fb = 1.0f / fallback_std(sqrtf(rms2_c));
-#pragma unroll
-            for (int j = 0; j < 8; ++j) u[j] = std_ok(var_c[j], rms2_c) ? __builtin_amdgcn_rsqf(var_c[j]) : fb;
-        }
-        // token step on B_ij = u_j Y_ij: r_i = std_j B_ij, w_i = 1 / r_i
-        float m[8], q = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) q = fmaf(u[j] * u[j], colsq[j], q);
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            float s = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s = fmaf(u[j], y[a][j], s);
-            m[a] = s;
-        }
-        token_sum8(m, q, sRed[buf], tid);
-        buf ^= 1;
-        rms2_r = q * kInvNN;
-        float dummy = 0.0f;
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            const float mean = m[a] * kInvN;
-            float s = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float d = fmaf(u[j], y[a][j], -mean);
-                s = fmaf(d, d, s);
-            }
-            var_r[a] = s;
-        }
-        token_sum8(var_r, dummy, sRed[buf], tid);
-        buf ^= 1;
-        {
-            const float fb = 1.0f / fallback_std(sqrtf(rms2_r));
-#pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                var_r[a] *= kInvN;
-                w[a] = std_ok(var_r[a], rms2_r) ? __builtin_amdgcn_rsqf(var_r[a]) : fb;
-            }
-        }
-    }
-
-    // ---- 4. second scale: g = r (K, per token) or c (V, per channel) --------------
-    // g from the last step with a correctly rounded sqrt (1 when no iteration ran),
-    // power-of-two gauge from the exponent of its mean, then FP8 E4M3.
-    float g[8];
-    {
-        const float rms2 = (AXIS == kAxisK) ? rms2_r : rms2_c;
-        const float fb = fallback_std(sqrtf(rms2));
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float var = (AXIS == kAxisK) ? var_r[k] : var_c[k];
-            g[k] = n_iter == 0 ? 1.0f : (std_ok(var, rms2) ? sqrtf(var) : fb);
-        }
-    }
-    float gsum = ((g[0] + g[1]) + (g[2] + g[3])) + ((g[4] + g[5]) + (g[6] + g[7]));
-    if constexpr (AXIS == kAxisK) {
-        gsum = sum_lanes16(gsum);                      // over the 16 token groups
-    } else {
-        float dummy8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        token_sum8(dummy8, gsum, sRed[buf], tid);      // over the 16 channel groups
-        buf ^= 1;
-    }
-    int gexp = (int)((__float_as_uint(gsum * kInvN) >> 23) & 255u) - 126;  // frexp exponent of the mean
-    gexp = gexp < -126 ? -126 : (gexp > 126 ? 126 : gexp);
-    const float gscale = pow2f(-gexp);
-    uint32_t s2code[8];
-    float inv_s2[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        uint32_t code = fp8_encode_nonneg(g[k] * gscale);
-        code = code < 1u ? 1u : code;                  // floor 2^-9
-        s2code[k] = code;
-        inv_s2[k] = __builtin_amdgcn_rcpf(fp8_decode_nonneg(code));
-    }
-
-    // ---- 5. Zn, group statistics, FP8 s1 / FP16 z ----------------------------------
+    // y = sig * sqrt(128) * Y for this lane's block (Y the normalised rotation)
+    float y2[8][8];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[a][j] *= (AXIS == kAxisK) ? inv_s2[a] : inv_s2[j];
+        for (int j = 0; j < 8; ++j) y2[a][j] = y[a][j] * y[a][j];
 
-    constexpr float kL = (float)R::kL;
-    float gmin[8], gmax[8];
-    if constexpr (AXIS == kAxisK) {                    // groups = channels, over tokens
+    // ---- 2. dual-axis normalisation ---------------------------------------------------
+    // Row factors wr = 1/r (per row, with squares wr2), column factors wc = sig/c'
+    // (c' = sqrt(128) c, the std of the stored scale) with squares wc2.
+    float wr[8], wr2[8], wc[8], wc2[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float lo = fminf(fminf(y[0][j], y[1][j]), fminf(y[2][j], y[3][j]));
-            float hi = fmaxf(fmaxf(y[0][j], y[1][j]), fmaxf(y[2][j], y[3][j]));
-            lo = fminf(lo, fminf(fminf(y[4][j], y[5][j]), fminf(y[6][j], y[7][j])));
-            hi = fmaxf(hi, fmaxf(fmaxf(y[4][j], y[5][j]), fmaxf(y[6][j], y[7][j])));
-            gmin[j] = min_lanes16(lo);
-            gmax[j] = max_lanes16(hi);
+    for (int k = 0; k < 8; ++k) wr[k] = 1.0f, wr2[k] = 1.0f;
+    float colsq[2] = {0.0f, 0.0f};   // sum_i y_ij^2 of the two owned columns
+    float gc[2] = {1.0f, 1.0f};      // c of the owned columns after the last channel step (V)
+    float gr = 1.0f;                 // r of the owned row after the last token step (K)
+    float last_rvar = 0.0f, last_rms2r = 0.0f;
+    int buf = 0;
+
+    for (int it = 0; it < n_iter; ++it) {
+        // channel step: moments of wr_i * y_ij over the 128 tokens
+        float t[4];
+        {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float s = 0.0f, q = 0.0f;
+#pragma unroll
+                for (int a = 0; a < 8; ++a) {
+                    s = fmaf(wr[a], y[a][j], s);
+                    q = fmaf(wr2[a], y2[a][j], q);
+                }
+                v[2 * j] = s, v[2 * j + 1] = q;
+            }
+            float z[4];
+            col_rs<OpSum, OpSum>(v, z);
+            cross_wave<OpSum, OpSum>(sm, buf, w, lane, z, t);
+            buf ^= 1;
         }
-    } else {                                           // groups = tokens, over channels
+        if (it == 0) colsq[0] = t[1], colsq[1] = t[3];
+        const float rms2 = wave_sum(t[1] + t[3]) * kInvNN;
+        float mean[2] = {t[0] * kInvN, t[2] * kInvN};
+        float var[2] = {fmaf(-mean[0], mean[0], t[1] * kInvN), fmaf(-mean[1], mean[1], t[3] * kInvN)};
+        if (wave_any(mean[0] * mean[0] > kCancel * var[0] || mean[1] * mean[1] > kCancel * var[1])) {
+            // exact centred second pass (uniform: every wave holds the same totals)
+            float m8[8], unused[8];
+            col_bcast(sm, w, cg, hl, make_float4(mean[0], 0.0f, mean[1], 0.0f), m8, unused);
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float q = 0.0f;
+#pragma unroll
+                for (int a = 0; a < 8; ++a) {
+                    const float d = fmaf(wr[a], y[a][j], -m8[j]);
+                    q = fmaf(d, d, q);
+                }
+                v[2 * j] = 0.0f, v[2 * j + 1] = q;
+            }
+            float z[4], t2[4];
+            col_rs<OpSum, OpSum>(v, z);
+            cross_wave<OpSum, OpSum>(sm, buf, w, lane, z, t2);
+            buf ^= 1;
+            var[0] = t2[1] * kInvN, var[1] = t2[3] * kInvN;
+        }
+        // degenerate rule on the stored scale (std floor 2^-60 * sqrt(128))
+        const float thr = kDegRel2 * rms2, floor2 = kDegAbs2 * 128.0f;
+        const bool rms_ok = rms2 >= floor2;
+        const float fb = rms_ok ? __builtin_amdgcn_rsqf(rms2) : kInvSqrtN;
+        float f[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) f[k] = step_factor(var[k], thr, floor2, fb);
+        if (AXIS == kAxisV && it == n_iter - 1) {
+            // c of the owned columns, unscaled: sqrt(var / 128) or rms / sqrt(128)
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                gc[k] = (var[k] > thr && var[k] >= floor2) ? sqrtf(var[k] * kInvN) : (rms_ok ? sqrtf(rms2 * kInvN) : 1.0f);
+            break;   // the final token step of V is absorbed into s1
+        }
+        col_bcast(sm, w, cg, hl, make_float4(sig * f[0], f[0] * f[0], sig * f[1], f[1] * f[1]), wc, wc2);
+        // rms of the token-step matrix: sum_j colsq_j * wc_j^2 / 128^2 (wave-local)
+        const float rms2r = wave_sum(fmaf(colsq[0], f[0] * f[0], colsq[1] * (f[1] * f[1]))) * kInvNN;
+
+        // token step: moments of wc_j * y_ij over the 128 channels
+        float rs[2];
+        {
+            float v[16];
+#pragma unroll
+            for (int a = 0; a < 8; ++a) {
+                float s = 0.0f, q = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    s = fmaf(wc[j], y[a][j], s);
+                    q = fmaf(wc2[j], y2[a][j], q);
+                }
+                v[2 * a] = s, v[2 * a + 1] = q;
+            }
+            row_rs<OpSum, OpSum>(v, cg, rs);
+        }
+        const float rmean = rs[0] * kInvN;
+        float rvar = fmaf(-rmean, rmean, rs[1] * kInvN);
+        if (wave_any(rmean * rmean > kCancel * rvar)) {
+            float m8[8], unused[8];
+            row_bcast(sm, w, rg, a_own, rmean, 0.0f, m8, unused);
+            float v[16];
+#pragma unroll
+            for (int a = 0; a < 8; ++a) {
+                float q = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float d = fmaf(wc[j], y[a][j], -m8[a]);
+                    q = fmaf(d, d, q);
+                }
+                v[2 * a] = 0.0f, v[2 * a + 1] = q;
+            }
+            float z2[2];
+            row_rs<OpSum, OpSum>(v, cg, z2);
+            rvar = z2[1] * kInvN;
+        }
+        const float fbr = rms2r >= kDegAbs2 ? __builtin_amdgcn_rsqf(rms2r) : 1.0f;
+        const float fr = step_factor(rvar, kDegRel2 * rms2r, kDegAbs2, fbr);
+        last_rvar = rvar, last_rms2r = rms2r;
+        row_bcast(sm, w, rg, a_own, fr, fr * fr, wr, wr2);
+    }
+    if (AXIS == kAxisK && n_iter > 0)   // r of the owned row after the last token step
+        gr = (last_rvar > kDegRel2 * last_rms2r && last_rvar >= kDegAbs2)
+                 ? sqrtf(last_rvar)
+                 : (last_rms2r >= kDegAbs2 ? sqrtf(last_rms2r) : 1.0f);
+
+    // ---- 3. second scale, Zn, group statistics --------------------------------------
+    constexpr float kL = (float)R::kL;
+    const int64_t rec_idx = dst_index ? dst_index[tile] : tile;
+    uint8_t* rec = packed + rec_idx * (int64_t)R::kBytes;
+    float inv_s1[8], zoff[8];   // per column (K) or per row (V) of this lane's block
+    if constexpr (AXIS == kAxisK) {
+        // gauge: mean of r over the 128 tokens (each row owned by a lane pair)
+        float part = wave_sum((cg & 1) ? 0.0f : gr);
+        if (lane == 0) sm.gsum[w] = part;
+        __syncthreads();
+        const float gmean = ((sm.gsum[0] + sm.gsum[1]) + (sm.gsum[2] + sm.gsum[3])) * kInvN;
+        int gexp = (int)((__float_as_uint(gmean) >> 23) & 255u) - 126;   // frexp exponent of the mean
+        gexp = gexp < -126 ? -126 : (gexp > 126 ? 126 : gexp);
+        uint32_t code = fp8_encode_nonneg(gr * pow2f(-gexp));
+        code = code < 1u ? 1u : code;                                    // floor 2^-9
+        if ((cg & 1) == 0) rec[R::kS2 + row0 + a_own] = (uint8_t)code;
+        const float m = __builtin_amdgcn_rcpf(fp8_decode_nonneg(code)) * kInvSqrtN;
+        float m8[8], unused[8];
+        row_bcast(sm, w, rg, a_own, m, 0.0f, m8, unused);
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
-            gmin[a] = fminf(fminf(fminf(y[a][0], y[a][1]), fminf(y[a][2], y[a][3])),
-                            fminf(fminf(y[a][4], y[a][5]), fminf(y[a][6], y[a][7])));
-            gmax[a] = fmaxf(fmaxf(fmaxf(y[a][0], y[a][1]), fmaxf(y[a][2], y[a][3])),
-                            fmaxf(fmaxf(y[a][4], y[a][5]), fmaxf(y[a][6], y[a][7])));
-        }
-        token_minmax8(gmin, gmax, sRed[buf], tid);
-        buf ^= 1;
-    }
-    uint32_t s1code[8], zbits[8];
-    float inv_s1[8], zoff[8];
+            const float ma = sig * m8[a];                                // the reader's sign
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        uint32_t code = fp8_encode_nonneg((gmax[k] - gmin[k]) * (1.0f / kL));
-        code = code < 1u ? 1u : code;                  // floor 2^-9
-        s1code[k] = code;
-        inv_s1[k] = __builtin_amdgcn_rcpf(fp8_decode_nonneg(code));
-        zbits[k] = f32_to_f16_bits_sat(gmin[k]);
-        zoff[k] = -f16_bits_to_f32(zbits[k]) * inv_s1[k];
+            for (int j = 0; j < 8; ++j) y[a][j] *= ma;                   // Zn
+        }
+        // per-column min / max over the 128 tokens
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float lo = y[0][j], hi = y[0][j];
+#pragma unroll
+            for (int a = 1; a < 8; ++a) lo = fminf(lo, y[a][j]), hi = fmaxf(hi, y[a][j]);
+            v[2 * j] = lo, v[2 * j + 1] = hi;
+        }
+        float z[4], t[4];
+        col_rs<OpMin, OpMax>(v, z);
+        cross_wave<OpMin, OpMax>(sm, buf, w, lane, z, t);
+        float pub[4];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t c1 = fp8_encode_nonneg((t[2 * k + 1] - t[2 * k]) * (1.0f / kL));
+            c1 = c1 < 1u ? 1u : c1;
+            const uint32_t zb = f32_to_f16_bits_sat(t[2 * k]);
+            const int ch = 8 * og + jc0 + k;
+            if (w == 0) {
+                rec[R::kS1 + ch] = (uint8_t)c1;
+                *reinterpret_cast<uint16_t*>(rec + R::kZ + 2 * ch) = (uint16_t)zb;
+            }
+            const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1));
+            pub[2 * k] = is1, pub[2 * k + 1] = -f16_bits_to_f32(zb) * is1;
+        }
+        col_bcast(sm, w, cg, hl, make_float4(pub[0], pub[1], pub[2], pub[3]), inv_s1, zoff);
+    } else {
+        // gauge: mean of c over the 128 channels (every wave holds all of them)
+        const float gmean = wave_sum(gc[0] + gc[1]) * kInvN;
+        int gexp = (int)((__float_as_uint(gmean) >> 23) & 255u) - 126;
+        gexp = gexp < -126 ? -126 : (gexp > 126 ? 126 : gexp);
+        const float gs = pow2f(-gexp);
+        float pub[4];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t code = fp8_encode_nonneg(gc[k] * gs);
+            code = code < 1u ? 1u : code;
+            if (w == 0) rec[R::kS2 + 8 * og + jc0 + k] = (uint8_t)code;
+            pub[2 * k] = sig * __builtin_amdgcn_rcpf(fp8_decode_nonneg(code)) * kInvSqrtN;
+            pub[2 * k + 1] = 0.0f;
+        }
+        float m8[8], unused[8];
+        col_bcast(sm, w, cg, hl, make_float4(pub[0], pub[1], pub[2], pub[3]), m8, unused);
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[a][j] *= m8[j];                // Zn
+        // per-token min / max over the 128 channels
+        float v[16];
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            float lo = y[a][0], hi = y[a][0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) lo = fminf(lo, y[a][j]), hi = fmaxf(hi, y[a][j]);
+            v[2 * a] = lo, v[2 * a + 1] = hi;
+        }
+        float z[2];
+        row_rs<OpMin, OpMax>(v, cg, z);
+        uint32_t c1 = fp8_encode_nonneg((z[1] - z[0]) * (1.0f / kL));
+        c1 = c1 < 1u ? 1u : c1;
+        const uint32_t zb = f32_to_f16_bits_sat(z[0]);
+        if ((cg & 1) == 0) {
+            const int tok = row0 + a_own;
+            rec[R::kS1 + tok] = (uint8_t)c1;
+            *reinterpret_cast<uint16_t*>(rec + R::kZ + 2 * tok) = (uint16_t)zb;
+        }
+        const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1));
+        row_bcast(sm, w, rg, a_own, is1, -f16_bits_to_f32(zb) * is1, inv_s1, zoff);
     }
 
-    // ---- 6. codes into the LDS record image, then 16-byte stores --------------------
-    // t = (Zn - z) / s1, clamped to [0, L]; adding 2^23 rounds it to the nearest
-    // integer (ties to even) in the low mantissa bits.
-    __syncthreads();                                   // everyone is done with sY as floats
-    uint8_t* img = reinterpret_cast<uint8_t*>(sY);
+    // ---- 4. codes -------------------------------------------------------------------
+    // t = (Zn - z) / s1 clamped to [0, L]; adding 2^23 rounds it to the nearest
+    // integer (ties to even) in the low mantissa bits.  The shifted sums of the
+    // 2^23 bit patterns are a constant, removed once per token.
+    constexpr uint32_t kBias = [] {
+        uint32_t c = 0;
+        for (int j = 0; j < 8; ++j) c += 0x4B000000u << (BITS * j);
+        return c;
+    }();
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
         uint32_t word = 0;
@@ -329,44 +543,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
             const int gi = (AXIS == kAxisK) ? j : a;
             float t = fmaf(y[a][j], inv_s1[gi], zoff[gi]);
             t = __builtin_amdgcn_fmed3f(t, 0.0f, kL) + kMagic;
-            word |= (__float_as_uint(t) - 0x4B000000u) << (BITS * j);
+            word += __float_as_uint(t) << (BITS * j);
         }
-        const int tok = 8 * tg + a;
+        word -= kBias;
+        uint8_t* dst = rec + (row0 + a) * R::kRowBytes;
         if constexpr (BITS == 2)
-            *reinterpret_cast<uint16_t*>(img + tok * R::kRowBytes + 2 * cg) = (uint16_t)word;
+            *reinterpret_cast<uint16_t*>(dst + 2 * og) = (uint16_t)word;
         else
-            *reinterpret_cast<uint32_t*>(img + tok * R::kRowBytes + 4 * cg) = word;
+            *reinterpret_cast<uint32_t*>(dst + 4 * og) = word;
     }
-    if constexpr (AXIS == kAxisK) {
-        if (tg == 0) {                                 // per-channel s1, z
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                img[R::kS1 + 8 * cg + j] = (uint8_t)s1code[j];
-                *reinterpret_cast<uint16_t*>(img + R::kZ + 2 * (8 * cg + j)) = (uint16_t)zbits[j];
-            }
-        }
-        if (cg == 0) {                                 // per-token s2
-#pragma unroll
-            for (int a = 0; a < 8; ++a) img[R::kS2 + 8 * tg + a] = (uint8_t)s2code[a];
-        }
-    } else {
-        if (cg == 0) {                                 // per-token s1, z
-#pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                img[R::kS1 + 8 * tg + a] = (uint8_t)s1code[a];
-                *reinterpret_cast<uint16_t*>(img + R::kZ + 2 * (8 * tg + a)) = (uint16_t)zbits[a];
-            }
-        }
-        if (tg == 0) {                                 // per-channel s2
-#pragma unroll
-            for (int j = 0; j < 8; ++j) img[R::kS2 + 8 * cg + j] = (uint8_t)s2code[j];
-        }
-    }
-    __syncthreads();
-    const int64_t rec = dst_index ? dst_index[tile] : tile;
-    uint4* dst = reinterpret_cast<uint4*>(packed + rec * R::kBytes);
-    const uint4* src = reinterpret_cast<const uint4*>(img);
-    for (int i = tid; i < R::kBytes / 16; i += 256) dst[i] = src[i];
 }
 
 template <int BITS, int AXIS>
