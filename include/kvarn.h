@@ -24,9 +24,14 @@
  *    quantised when it fills (pheeree.github.io blog, part 3; dimensionstp
  *    review, section 3-2(1): one 128-token block is one tile).
  *  - Packed record of one tile, kvarn_tile_bytes(bits) bytes, 16-byte aligned:
- *      [0, 2048*b)          codes, token-major: token t owns bytes
- *                           [16*b*t, 16*b*(t+1)); channel c is at byte
- *                           16*b*t + c*b/8, bit (c*b)%8, least significant first
+ *      [0, 2048*b)          codes, 128 rows of 16*b bytes.  Row r belongs to
+ *                           index r of the s2 axis: token r for K, channel r
+ *                           for V.  Within row r the code of group g (K:
+ *                           channel g, V: token g) is at byte 16*b*r + g*b/8,
+ *                           bit (g*b)%8, least significant first.  (Each
+ *                           reader then finds the 32 codes of one row that a
+ *                           decode contraction needs in 8 contiguous bytes:
+ *                           a token's channels for K, a channel's tokens for V.)
  *      [2048*b, +128)       s1, FP8 E4M3 (OCP), one per group
  *      [2048*b + 128, +128) s2, FP8 E4M3, one per index of the other axis
  *      [2048*b + 256, +256) z, IEEE FP16 little-endian, one per group
@@ -58,7 +63,7 @@ extern "C" {
 
 #define KVARN_HEAD_DIM 128
 #define KVARN_TILE_TOKENS 128
-#define KVARN_FORMAT_VERSION 1
+#define KVARN_FORMAT_VERSION 2
 
 /* Status codes returned by the entry points. */
 enum {

@@ -5,18 +5,28 @@
 // Dequantization Overhead; dimensionstp review, section 4-2).  Because the
 // rotation H/sqrt(128) is orthogonal and symmetric, attention runs in the
 // rotated domain and never rebuilds K or V:
-//     q . Xh_t  =  (H q) . Yh_t          sum_t p_t Xh_t  =  (sum_t p_t Yh_t) H
+//     q . Xh_t  =  (H q / sqrt(128)) . Yh_t      sum_t p_t Xh_t  =  (sum_t p_t Yh_t) H / sqrt(128)
 // and with K: Yh_tc = s2_t (code_tc s1_c + z_c),  V: Yh_tc = s2_c (code_tc s1_t + z_t)
 //     score_t = s2_t * ( sum_c (q~_c s1_c) code_tc + sum_c q~_c z_c )
-//     acc_c  += s2_c * ( sum_t (p_t s1_t) code_tc + sum_t p_t z_t )
+//     out_c  += s2_c * ( sum_t (p_t s1_t) code_tc + sum_t p_t z_t )
 //
-// Kernel 1 (partials): grid (split, KV head, sequence), 256 threads.  Every
-// wave owns 32 of the 128 tokens of each tile and keeps its own running max,
-// sum and accumulator (flash-decoding style), so tiles need no block-wide
-// synchronisation; the four waves are merged once at the end of the split.
-// Lane = (token group tg: 8 tokens) x (channel group cg: 8 channels); scores
-// reduce over the 16 cg lanes, values over the 4 tg lanes.
-// Kernel 2 (combine): log-sum-exp merge of the splits, inverse rotation, FP16.
+// Both sums over codes are dense contractions (4 query heads x 128 x 128 per
+// tile) and run on the matrix cores with v_mfma_scale_f32_16x16x128_f8f6f4:
+//   B = the codes straight from the record: a 2-bit code c masked into an E2M1
+//       nibble reads as c/2 (block scale 2^1), a 4-bit code masked into an E4M3
+//       byte as c * 2^-9 (block scale 2^9) -- both exact.  A record row holds
+//       the 128 codes of one s2 index (a token of K, a channel of V), so the 32
+//       codes one lane feeds are 8 contiguous bytes.
+//   A = the 4 queries' q~ s1 (scores, four pieces) or p s1 (values, three
+//       pieces) as FP8 E4M3 pieces, x = P0 + P1/16 + P2/256 (+ P3/4096), every
+//       piece the nearest E4M3 value of what the earlier pieces left, times 16;
+//       rows are (query, piece) with the block scale 2^-4k of piece k, and the
+//       matrix core sums the pieces in fp32.  The representation error of x is
+//       at most 2^-16 (scores) or 2^-12 (weights) of |x|.
+// Every wave owns a range of tiles of one (sequence, KV head, 4-query chunk)
+// and keeps its own running max, sum and accumulator (flash-decoding); the
+// waves' partials are merged by a second kernel that also applies the inverse
+// rotation and rounds to FP16.
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
 
@@ -25,201 +35,407 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPart = 2 + kN;  // m (log2 domain), l, acc[128] per (sequence, query head, split)
+constexpr int kPiecesQ = 4;   // query pieces: score error ~2^-17 relative per product
+constexpr int kPiecesP = 3;   // weight pieces
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+// Same 16-lane Hadamard network as the quantiser: lane cg ends with output
+// group out_group(cg) times the sign mask_sign(kWhtSigma, cg).
+constexpr uint32_t kWhtS1 = 0x5a5a, kWhtS2 = 0x3c3c, kWhtS3 = 0xff00, kWhtS4 = 0x9696, kWhtSigma = 0x09f6;
+__device__ __forceinline__ int out_group(int cg) { return (cg & 4) ? (cg ^ 3) : cg; }
+__device__ __forceinline__ float mask_sign(uint32_t mask, int cg) { return ((mask >> cg) & 1u) ? -1.0f : 1.0f; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    return v + dpp<kDppMirror>(v);
+}
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    return fmaxf(v, dpp<kDppMirror>(v));
+}
+
+// The 8 registers of an A or B operand of v_mfma_*_16x16x128_f8f6f4 hold, in
+// lane l, row/column l%16 and the 32 K-slots of lane group gl = l/16.  For
+// E4M3 operands slot s is k = 16 gl + s (s < 16) or 64 + 16 gl + s - 16; for
+// E2M1 operands slot s is k = 32 gl + s (nibbles low first).  The code loads
+// below put record positions (channels of a K row, tokens of a V row) into
+// slots in the order of the mask-based widening, so position x of the 128 sits
+// at k = kpos<BITS>(x); the A writer places a piece of position x at the E4M3
+// slot of that k.
 template <int BITS>
-__device__ __forceinline__ void load_codes8x8(const uint8_t* __restrict__ rec, int tok0, int cg,
-                                              float (&code)[8][8]) {
+__device__ __forceinline__ int kpos(int x) {
+    if constexpr (BITS == 2) {
+        // lane group x/32 loads 8 bytes; & 0x33333333 gives slots 0-7 = even
+        // positions 0..14, >> 2 slots 8-15 = odd ones; the second dword likewise
+        const int o = x & 31;
+        return 32 * (x >> 5) + 16 * (o >> 4) + 8 * (o & 1) + ((o & 15) >> 1);
+    } else {
+        // E4M3 slots: lane group gl loads positions 16gl..16gl+15 into slots
+        // 0-15 and 64+16gl.. into slots 16-31, each 8 bytes widened as
+        // [& 0x0F0F0F0F, >> 4 & ..] per dword
+        const int o = x & 15;
+        const int s = 8 * (o >> 3) + 4 * (o & 1) + ((o & 7) >> 1);
+        return (x & ~15) + s;   // k = 16 gl + s (+64): same k as the position's chunk
+    }
+}
+// E4M3 slot (lane group, byte) of a K index k.
+__device__ __forceinline__ void fp8_slot(int k, int& gl, int& s) {
+    gl = (k & 63) >> 4;
+    s = (k & 15) + 16 * (k >> 6);
+}
+
+// Buffer resource over one record (num_records = 0 turns every load into a
+// zero with no memory access: used for tiles past the end or with an invalid
+// block-table entry, so that every iteration issues the same loads).
+constexpr int kRsrcWord3 = 0x00020000;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), (short)0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Load the 32 codes of record row `row` that lane group gl feeds (8 bytes for
+// 2 bits, two times 8 bytes for 4 bits).
+template <int BITS>
+__device__ __forceinline__ uint4 load_row_codes(__amdgpu_buffer_rsrc_t r, int row, int gl) {
     using R = Rec<BITS>;
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        uint32_t word;
-        if constexpr (BITS == 2)
-            word = *reinterpret_cast<const uint16_t*>(rec + (tok0 + a) * R::kRowBytes + 2 * cg);
-        else
-            word = *reinterpret_cast<const uint32_t*>(rec + (tok0 + a) * R::kRowBytes + 4 * cg);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) code[a][j] = (float)((word >> (BITS * j)) & ((1u << BITS) - 1u));
+    const int p = row * R::kRowBytes + 8 * gl;
+    if constexpr (BITS == 2) {
+        const uint2 a = ld8(r, p);
+        return make_uint4(a.x, a.y, 0u, 0u);
+    } else {
+        const uint2 a = ld8(r, p), b = ld8(r, p + 32);
+        return make_uint4(a.x, a.y, b.x, b.y);
     }
 }
 
-__device__ __forceinline__ void load_fp8x8(const uint8_t* p, float (&v)[8]) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
+// Widen raw code bytes into an f8f6f4 operand (E2M1 for 2 bits, E4M3 for 4).
+template <int BITS>
+__device__ __forceinline__ v8i widen(uint4 r) {
+    v8i o;
+    if constexpr (BITS == 2) {
+        o[0] = (int)(r.x & 0x33333333u), o[1] = (int)((r.x >> 2) & 0x33333333u);
+        o[2] = (int)(r.y & 0x33333333u), o[3] = (int)((r.y >> 2) & 0x33333333u);
+        o[4] = 0, o[5] = 0, o[6] = 0, o[7] = 0;
+    } else {
+        o[0] = (int)(r.x & 0x0F0F0F0Fu), o[1] = (int)((r.x >> 4) & 0x0F0F0F0Fu);
+        o[2] = (int)(r.y & 0x0F0F0F0Fu), o[3] = (int)((r.y >> 4) & 0x0F0F0F0Fu);
+        o[4] = (int)(r.z & 0x0F0F0F0Fu), o[5] = (int)((r.z >> 4) & 0x0F0F0F0Fu);
+        o[6] = (int)(r.w & 0x0F0F0F0Fu), o[7] = (int)((r.w >> 4) & 0x0F0F0F0Fu);
+    }
+    return o;
+}
+
+__device__ __forceinline__ void fp8x8(uint2 b, float (&v)[8]) {
+    f2 p;
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(b.x, false); v[0] = p.x, v[1] = p.y;
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(b.x, true); v[2] = p.x, v[3] = p.y;
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(b.y, false); v[4] = p.x, v[5] = p.y;
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(b.y, true); v[6] = p.x, v[7] = p.y;
+}
+__device__ __forceinline__ void f16x8(uint4 b, float (&v)[8]) {
+    const uint32_t w[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        v[k] = fp8_decode_nonneg((w.x >> (8 * k)) & 0xFFu);
-        v[4 + k] = fp8_decode_nonneg((w.y >> (8 * k)) & 0xFFu);
+    for (int k = 0; k < 4; ++k) v[2 * k] = f16_bits_to_f32(w[k] & 0xFFFFu), v[2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
+}
+
+// Split 8 values (positions 8J..8J+7 of the lane's query) into PIECES E4M3
+// pieces and write them as dwords into the A staging buffer of the wave
+// (64 lanes x 32 bytes; rows m = 4 query + piece).  off_e / off_o: byte offsets
+// of the piece-0 dword of the even / odd positions.
+template <int PIECES>
+__device__ __forceinline__ void write_pieces(uint8_t* __restrict__ stage, int off_e, int off_o, const float (&u0)[8]) {
+    float u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = u0[i];
+#pragma unroll
+    for (int k = 0; k < PIECES; ++k) {
+        int e = 0, o = 0;
+        e = __builtin_amdgcn_cvt_pk_fp8_f32(u[0], u[2], e, false);
+        e = __builtin_amdgcn_cvt_pk_fp8_f32(u[4], u[6], e, true);
+        o = __builtin_amdgcn_cvt_pk_fp8_f32(u[1], u[3], o, false);
+        o = __builtin_amdgcn_cvt_pk_fp8_f32(u[5], u[7], o, true);
+        *reinterpret_cast<int*>(stage + off_e + 32 * k) = e;
+        *reinterpret_cast<int*>(stage + off_o + 32 * k) = o;
+        if (k + 1 < PIECES) {
+            f2 b;
+            b = __builtin_amdgcn_cvt_pk_f32_fp8(e, false); u[0] = 16.0f * (u[0] - b.x), u[2] = 16.0f * (u[2] - b.y);
+            b = __builtin_amdgcn_cvt_pk_f32_fp8(e, true); u[4] = 16.0f * (u[4] - b.x), u[6] = 16.0f * (u[6] - b.y);
+            b = __builtin_amdgcn_cvt_pk_f32_fp8(o, false); u[1] = 16.0f * (u[1] - b.x), u[3] = 16.0f * (u[3] - b.y);
+            b = __builtin_amdgcn_cvt_pk_f32_fp8(o, true); u[5] = 16.0f * (u[5] - b.x), u[7] = 16.0f * (u[7] - b.y);
+        }
     }
 }
 
-__device__ __forceinline__ void load_f16x8(const uint8_t* p, float (&v)[8]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        v[2 * k] = f16_bits_to_f32(a[k] & 0xFFFFu);
-        v[2 * k + 1] = f16_bits_to_f32(a[k] >> 16);
-    }
+// Byte offsets in the A staging buffer of the piece-0 dwords of positions
+// {x0, x0+2, x0+4, x0+6} (x0 = 8J or 8J+1) for query qg.
+template <int BITS>
+__device__ __forceinline__ int piece_offset(int x0, int qg) {
+    int gl, s;
+    fp8_slot(kpos<BITS>(x0), gl, s);
+    return (16 * gl + 4 * qg) * 32 + s;
 }
 
-template <int BK, int BV, int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(
+// Raw bytes of one K/V tile pair as one lane needs them.
+struct TileRaw {
+    uint4 kc[8], vc[8];          // codes of record rows 8n + blk (lane group's 8 or 16 bytes)
+    uint2 ks1, ks2, vs1, vs2;    // FP8 scales: K s1 of channels 8G.., K s2 / V s1 of tokens 8n.., V s2 of channels 8n..
+    uint4 kz, vz;                // FP16 zero-points: K of channels 8G.., V of tokens 8n..
+};
+
+struct WaveSmem {
+    uint8_t qa[64 * 32];   // A operand staging: query pieces (scores)
+    uint8_t pa[64 * 32];   // A operand staging: weight pieces (values)
+};
+
+template <int BK, int BV>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ n_tiles_per_seq, int64_t n_records,
-    int n_q_heads, int n_kv_heads, int max_tiles, int tiles_per_split, int n_splits, int gs, float scale_log2,
-    float* __restrict__ ws) {
+    int n_q_heads, int n_kv_heads, int max_tiles, int tiles_per_split, int n_splits, int gs, int n_chunks,
+    float scale_log2, float* __restrict__ ws) {
     using RK = Rec<BK>;
     using RV = Rec<BV>;
-    __shared__ __align__(16) float sQ[G][kN];
-    __shared__ __align__(16) float sMerge[4][G][kPart];
+    __shared__ WaveSmem smem[4];
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int tg = lane >> 4, cg = lane & 15;
-    const int split = blockIdx.x, kvh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform per wave
+    const int split = 4 * blockIdx.x + w;
+    if (split >= n_splits) return;                     // uniform per wave; no workgroup barriers below
+    const int kvh = blockIdx.y / n_chunks, chunk = blockIdx.y % n_chunks;
     const int64_t b = blockIdx.z;
-    const int hq0 = kvh * gs;
+    const int qg = lane >> 4, n = lane & 15;           // query of the lane, column within a block
+    const int hq = kvh * gs + 4 * chunk + qg;          // this lane's query head
+    const bool q_ok = 4 * chunk + qg < gs;
+    WaveSmem& sm = smem[w];
 
-    // rotated queries q~ = H q / sqrt(128) (heads g >= gs are zero padding)
-    for (int i = tid; i < G * kN; i += 256) {
-        const int g = i / kN, d = i % kN;
-        sQ[g][d] = g < gs ? f16_bits_to_f32(q[(b * n_q_heads + hq0 + g) * kN + d]) : 0.0f;
-    }
-    __syncthreads();
-    for (int s = 1; s < kN; s <<= 1) {
-        for (int i = tid; i < G * kN / 2; i += 256) {
-            const int g = i / (kN / 2), p = i % (kN / 2);
-            const int lo = (p / s) * 2 * s + (p % s), hi = lo + s;
-            const float a = sQ[g][lo], c = sQ[g][hi];
-            sQ[g][lo] = a + c;
-            sQ[g][hi] = a - c;
+    // ---- rotated, scaled queries: lane holds channels 8*G..8*G+7 of query qg --
+    const int G = out_group(n);
+    float qh[8];
+    float qexp;                                        // q~ = qh * 2^qexp
+    {
+        float v[8];
+        if (q_ok) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(q + ((b * n_q_heads + hq) * kN + 8 * n));
+            f16x8(raw, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
         }
-        __syncthreads();
+        fwht_regs<8>(v);
+        const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
+        const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppXor1>(v[i]), s1, v[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppXor2>(v[i]), s2, v[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<0x128>(v[i]), s3, v[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppHalfMirror>(v[i]), s4, v[i]);
+        const float sg = mask_sign(kWhtSigma, n) * kInvSqrtN;
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= sg, mx = fmaxf(mx, fabsf(v[i]));
+        mx = row_max16(mx);
+        const int e = mx > 0.0f ? (int)((__float_as_uint(mx) >> 23) & 255u) - 126 : 0;   // mx in [2^(e-1), 2^e)
+        qexp = (float)e;
+        const float sc = pow2f(-e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qh[i] = v[i] * sc;                       // |qh| < 1
     }
-    float qt[G][8];
+    // A-operand block scale of this lane's row (query lane/4 of the rows, piece lane%4)
+    int scale_q, scale_p;
+    {
+        const int m = lane & 15, rq = m >> 2, piece = m & 3;
+        const int e = __builtin_amdgcn_ds_bpermute(4 * (16 * rq), (int)qexp);
+        scale_q = 127 + e - 4 * piece;
+        scale_p = 127 - 4 * piece;
+    }
+    constexpr int kScaleB_K = BK == 2 ? 128 : 136, kScaleB_V = BV == 2 ? 128 : 136;
+    constexpr int kFmtK = BK == 2 ? 4 : 0, kFmtV = BV == 2 ? 4 : 0;
+    // staging offsets: scores pieces for channels 8G.. ; weight pieces for tokens 8n..
+    const int qoff_e = piece_offset<BK>(8 * G, qg), qoff_o = piece_offset<BK>(8 * G + 1, qg);
+    const int poff_e = piece_offset<BV>(8 * n, qg), poff_o = piece_offset<BV>(8 * n + 1, qg);
+    // rows of unused pieces (piece 3 of the weights) stay zero
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qt[g][j] = sQ[g][8 * cg + j] * kInvSqrtN;
+    for (int i = 0; i < 8; ++i) {
+        reinterpret_cast<int*>(sm.qa)[lane * 8 + i] = 0;
+        reinterpret_cast<int*>(sm.pa)[lane * 8 + i] = 0;
+    }
+    __builtin_amdgcn_wave_barrier();
 
-    float m[G], l[G], acc[G][8];
+    float m_run = -INFINITY, l_run = 0.0f, acc[8];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g] = -INFINITY;
-        l[g] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
-    }
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 
     int nt = n_tiles_per_seq[b];
     nt = nt < 0 ? 0 : (nt > max_tiles ? max_tiles : nt);
     const int j0 = split * tiles_per_split;
     const int j1 = min(j0 + tiles_per_split, nt);
-    const int tok0 = 32 * w + 8 * tg;  // first of this lane's 8 tokens within a tile
+    const int gl = lane >> 4;                            // lane group of the B operand
+    const int64_t row_base = ((int64_t)b * n_kv_heads + kvh) * max_tiles;
+    const float e2 = pow2f((int)qexp);                  // 2^exponent of the query scaling
 
-    for (int j = j0; j < j1; ++j) {
-        const int64_t row = ((int64_t)b * n_kv_heads + kvh) * max_tiles + j;
-        const int64_t idx = block_table ? (int64_t)block_table[row] : row;
-        if (idx < 0 || idx >= n_records) continue;     // uniform over the workgroup
-        // ---------------- scores from the K record
-        const uint8_t* kr = kp + idx * RK::kBytes;
-        float s1[8], z[8], s2[8], code[8][8];
-        load_fp8x8(kr + RK::kS1 + 8 * cg, s1);
-        load_f16x8(kr + RK::kZ + 16 * cg, z);
-        load_fp8x8(kr + RK::kS2 + tok0, s2);
-        load_codes8x8<BK>(kr, tok0, cg, code);
-        float sc[G][8];
+    // record index of tile j of this (sequence, KV head), or -1 when j is past the
+    // wave's range or the block-table entry is outside the record buffer
+    auto record_of = [&](int j) -> int64_t {
+        if (j >= j1) return -1;
+        const int64_t idx = block_table ? (int64_t)block_table[row_base + j] : row_base + j;
+        return (idx >= 0 && idx < n_records) ? idx : -1;    // uniform per wave
+    };
+    auto load = [&](int64_t idx, TileRaw& t) {
+        const bool ok = idx >= 0;
+        const __amdgpu_buffer_rsrc_t rk = record_rsrc(kp + (ok ? idx : 0) * RK::kBytes, ok ? RK::kBytes : 0);
+        const __amdgpu_buffer_rsrc_t rv = record_rsrc(vp + (ok ? idx : 0) * RV::kBytes, ok ? RV::kBytes : 0);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float cpart = 0.0f, qs[8];
+        for (int blk = 0; blk < 8; ++blk) t.kc[blk] = load_row_codes<BK>(rk, 8 * n + blk, gl);
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                qs[jj] = qt[g][jj] * s1[jj];
-                cpart = fmaf(qt[g][jj], z[jj], cpart);
+        for (int blk = 0; blk < 8; ++blk) t.vc[blk] = load_row_codes<BV>(rv, 8 * n + blk, gl);
+        t.ks1 = ld8(rk, RK::kS1 + 8 * G);
+        t.kz = ld16(rk, RK::kZ + 16 * G);
+        t.ks2 = ld8(rk, RK::kS2 + 8 * n);
+        t.vs1 = ld8(rv, RV::kS1 + 8 * n);
+        t.vz = ld16(rv, RV::kZ + 16 * n);
+        t.vs2 = ld8(rv, RV::kS2 + 8 * n);
+    };
+    auto compute = [&](const TileRaw& t) {
+        // ---- query pieces q~_c s1_c (channels 8G..8G+7 of query qg) and z term
+        float cz;
+        {
+            float s1[8], z[8], u[8];
+            fp8x8(t.ks1, s1);
+            f16x8(t.kz, z);
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] = qh[i] * s1[i], part = fmaf(qh[i], z[i], part);
+            cz = row_sum16(part);                          // sum_c qh_c z_c over the query's 128 channels
+            write_pieces<kPiecesQ>(sm.qa, qoff_e, qoff_o, u);
+        }
+        __builtin_amdgcn_wave_barrier();
+        v8i aq;
+        {
+            const int4 x0 = *reinterpret_cast<const int4*>(sm.qa + 32 * lane);
+            const int4 x1 = *reinterpret_cast<const int4*>(sm.qa + 32 * lane + 16);
+            aq[0] = x0.x, aq[1] = x0.y, aq[2] = x0.z, aq[3] = x0.w, aq[4] = x1.x, aq[5] = x1.y, aq[6] = x1.z, aq[7] = x1.w;
+        }
+        // ---- scores of tokens 8n + blk for query qg
+        float sc[8];
+        {
+            float s2[8];
+            fp8x8(t.ks2, s2);
+            v4f d[8];   // eight independent products, issued back to back
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) {
+                const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                d[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq, widen<BK>(t.kc[blk]), zero, 0, kFmtK, 0,
+                                                                           scale_q, 0, kScaleB_K);
             }
-            const float cz = sum_lanes16(cpart);
+            const float cze = cz * e2;
 #pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                float d = 0.0f;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) d = fmaf(qs[jj], code[a][jj], d);
-                sc[g][a] = (sum_lanes16(d) + cz) * s2[a] * scale_log2;
+            for (int blk = 0; blk < 8; ++blk) {
+                // rows of the lane: query qg, pieces 0..3
+                const float raw = (d[blk][0] + d[blk][1]) + (d[blk][2] + d[blk][3]);
+                sc[blk] = (raw + cze) * (s2[blk] * scale_log2);
             }
         }
-        // ---------------- online softmax (per wave)
-        float p[G][8], alpha[G];
+        // ---- online softmax over this tile (per query: the 16 lanes of a row)
+        float mt = sc[0];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float mx = sc[g][0];
+        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
+        mt = row_max16(mt);
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile (m_run = -inf)
+        float p[8], ps = 0.0f;
 #pragma unroll
-            for (int a = 1; a < 8; ++a) mx = fmaxf(mx, sc[g][a]);
-            mx = max_lanes_hi(mx);
-            const float mnew = fmaxf(m[g], mx);
-            alpha[g] = exp2f(m[g] - mnew);             // m = -inf on the first tile -> 0
-            float ps = 0.0f;
+        for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new), ps += p[i];
+        l_run = fmaf(l_run, alpha, row_sum16(ps));
+        m_run = m_new;
+        // ---- weight pieces p_t s1_t (tokens 8n..8n+7) and z term
+        float zs;
+        {
+            float s1[8], z[8], u[8];
+            fp8x8(t.vs1, s1);
+            f16x8(t.vz, z);
+            float part = 0.0f;
 #pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                p[g][a] = exp2f(sc[g][a] - mnew);
-                ps += p[g][a];
-            }
-            l[g] = l[g] * alpha[g] + sum_lanes_hi(ps);
-            m[g] = mnew;
+            for (int i = 0; i < 8; ++i) u[i] = p[i] * s1[i], part = fmaf(p[i], z[i], part);
+            zs = row_sum16(part);
+            write_pieces<kPiecesP>(sm.pa, poff_e, poff_o, u);
         }
-        // ---------------- weighted values from the V record
-        const uint8_t* vr = vp + idx * RV::kBytes;
-        float vs1[8], vz[8], vs2[8];
-        load_fp8x8(vr + RV::kS1 + tok0, vs1);
-        load_f16x8(vr + RV::kZ + 2 * tok0, vz);
-        load_fp8x8(vr + RV::kS2 + 8 * cg, vs2);
-        load_codes8x8<BV>(vr, tok0, cg, code);
+        __builtin_amdgcn_wave_barrier();
+        v8i ap;
+        {
+            const int4 x0 = *reinterpret_cast<const int4*>(sm.pa + 32 * lane);
+            const int4 x1 = *reinterpret_cast<const int4*>(sm.pa + 32 * lane + 16);
+            ap[0] = x0.x, ap[1] = x0.y, ap[2] = x0.z, ap[3] = x0.w, ap[4] = x1.x, ap[5] = x1.y, ap[6] = x1.z, ap[7] = x1.w;
+        }
+        // ---- values: channels 8n + blk for query qg
+        {
+            float s2[8];
+            fp8x8(t.vs2, s2);
+            v4f d[8];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float zs = 0.0f, pw[8];
-#pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                pw[a] = p[g][a] * vs1[a];
-                zs = fmaf(p[g][a], vz[a], zs);
+            for (int blk = 0; blk < 8; ++blk) {
+                const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                d[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ap, widen<BV>(t.vc[blk]), zero, 0, kFmtV, 0,
+                                                                           scale_p, 0, kScaleB_V);
             }
-            zs = sum_lanes_hi(zs);
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                float d = 0.0f;
-#pragma unroll
-                for (int a = 0; a < 8; ++a) d = fmaf(pw[a], code[a][jj], d);
-                acc[g][jj] = fmaf(acc[g][jj], alpha[g], vs2[jj] * (sum_lanes_hi(d) + zs));
+            for (int blk = 0; blk < 8; ++blk) {
+                const float raw = (d[blk][0] + d[blk][1]) + d[blk][2];   // piece row 3 of the weights is zero
+                acc[blk] = fmaf(acc[blk], alpha, s2[blk] * (raw + zs));
             }
         }
+        __builtin_amdgcn_wave_barrier();                 // staging buffers are rewritten next tile
+    };
+
+    // software pipeline: the next tile's loads are in flight while one is
+    // computed; every iteration issues the same loads (tiles without a record
+    // read zeros without touching memory) so the load counters stay exact.
+    TileRaw ta, tb;
+    int64_t ia = record_of(j0), ib;
+    load(ia, ta);
+    for (int j = j0; j < j1; j += 2) {
+        ib = record_of(j + 1);
+        load(ib, tb);
+        if (ia >= 0) compute(ta);
+        ia = record_of(j + 2);
+        load(ia, ta);
+        if (ib >= 0) compute(tb);
     }
 
-    // ---------------- merge the four waves, write this split's partial
-    if (tg == 0) {
+    // ---- this wave's partial: m, l, acc[channels 8n..8n+7] of query qg
+    if (q_ok) {
+        float* dst = ws + ((b * n_q_heads + hq) * n_splits + split) * kPart;
+        if (n == 0) dst[0] = m_run, dst[1] = l_run;
+        float* a = dst + 2 + 8 * n;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (cg == 0) {
-                sMerge[w][g][0] = m[g];
-                sMerge[w][g][1] = l[g];
-            }
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) sMerge[w][g][2 + 8 * cg + jj] = acc[g][jj];
-        }
-    }
-    __syncthreads();
-    for (int i = tid; i < gs * kPart; i += 256) {
-        const int g = i / kPart, e = i % kPart;
-        const float M = fmaxf(fmaxf(sMerge[0][g][0], sMerge[1][g][0]), fmaxf(sMerge[2][g][0], sMerge[3][g][0]));
-        float val;
-        if (e == 0) {
-            val = M;
-        } else if (M == -INFINITY) {
-            val = 0.0f;                                 // no tokens in this split
-        } else {
-            val = 0.0f;
-#pragma unroll
-            for (int ww = 0; ww < 4; ++ww) val += sMerge[ww][g][e] * exp2f(sMerge[ww][g][0] - M);
-        }
-        ws[((b * n_q_heads + hq0 + g) * n_splits + split) * kPart + e] = val;
+        for (int i = 0; i < 8; ++i) a[i] = acc[i];
     }
 }
 
-// One workgroup of 128 threads per (sequence, query head).
+// One workgroup of 128 threads per (sequence, query head): log-sum-exp merge of
+// the splits, inverse rotation, FP16.
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws, int n_splits,
                                                              uint16_t* __restrict__ out) {
     __shared__ float sO[kN];
@@ -231,7 +447,9 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
     float L = 0.0f, A = 0.0f;
     if (M != -INFINITY) {
         for (int s = 0; s < n_splits; ++s) {
-            const float f = exp2f(p[s * kPart] - M);
+            const float ms = p[s * kPart];
+            if (ms == -INFINITY) continue;              // split without tokens
+            const float f = exp2f(ms - M);
             L = fmaf(p[s * kPart + 1], f, L);
             A = fmaf(p[s * kPart + 2 + d], f, A);
         }
@@ -247,34 +465,31 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
     out[row * kN + d] = (uint16_t)f32_to_f16_bits_sat(sO[d] * kInvSqrtN);
 }
 
-template <int BK, int BV, int G>
-hipError_t launch_partial(const DecodeArgs& a, int gs) {
-    const dim3 grid((unsigned)a.n_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch), block(256);
-    decode_partial_kernel<BK, BV, G><<<grid, block, 0, a.stream>>>(
-        a.q, a.k_packed, a.v_packed, a.block_table, a.n_tiles_per_seq, a.n_records, a.n_q_heads, a.n_kv_heads,
-        a.max_tiles, a.tiles_per_split, a.n_splits, gs, a.sm_scale * kLog2e, a.workspace);
-    return hipGetLastError();
-}
-
 template <int BK, int BV>
 hipError_t launch_bits(const DecodeArgs& a) {
     const int gs = a.n_q_heads / a.n_kv_heads;
-    if (gs <= 1) return launch_partial<BK, BV, 1>(a, gs);
-    if (gs <= 2) return launch_partial<BK, BV, 2>(a, gs);
-    if (gs <= 4) return launch_partial<BK, BV, 4>(a, gs);
-    return launch_partial<BK, BV, 8>(a, gs);
+    const int n_chunks = (gs + 3) / 4;
+    const dim3 grid((unsigned)((a.n_splits + 3) / 4), (unsigned)(a.n_kv_heads * n_chunks), (unsigned)a.batch);
+    decode_mfma_kernel<BK, BV><<<grid, dim3(256), 0, a.stream>>>(
+        a.q, a.k_packed, a.v_packed, a.block_table, a.n_tiles_per_seq, a.n_records, a.n_q_heads, a.n_kv_heads,
+        a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-void decode_split_plan(int64_t batch, int n_kv_heads, int max_tiles, int* n_splits, int* tiles_per_split) {
+// Split-K plan: tiles of one (sequence, KV head) are cut into n_splits ranges
+// of tiles_per_split tiles, one wave each, aiming at about 8 waves per CU.
+void decode_split_plan(int64_t batch, int n_kv_heads, int n_q_heads, int max_tiles, int* n_splits,
+                       int* tiles_per_split) {
     if (max_tiles <= 0) {
         *n_splits = 1;
         *tiles_per_split = 1;
         return;
     }
-    const int64_t heads = batch * (int64_t)n_kv_heads;
-    int64_t want = heads > 0 ? (2048 + heads - 1) / heads : 1;  // aim for ~8 workgroups per CU
+    const int gs = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 1;
+    const int64_t heads = batch * (int64_t)n_kv_heads * ((gs + 3) / 4);
+    int64_t want = heads > 0 ? (2048 + heads - 1) / heads : 1;
     if (want < 1) want = 1;
     if (want > max_tiles) want = max_tiles;
     const int tps = (int)((max_tiles + want - 1) / want);

@@ -103,7 +103,7 @@ int kvarn_dequantize_tiles(const void* packed, const int64_t* src_tile_index, in
 size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_heads, int max_tiles) {
     if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0) return 0;
     int n_splits = 1, tps = 1;
-    kvarn::decode_split_plan(batch, n_kv_heads, max_tiles, &n_splits, &tps);
+    kvarn::decode_split_plan(batch, n_kv_heads, n_q_heads, max_tiles, &n_splits, &tps);
     return (size_t)batch * (size_t)n_q_heads * (size_t)n_splits * (size_t)(2 + KVARN_HEAD_DIM) * sizeof(float);
 }
 
@@ -142,7 +142,7 @@ int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed,
     a.out = static_cast<uint16_t*>(out);
     a.workspace = static_cast<float*>(workspace);
     a.stream = stream;
-    kvarn::decode_split_plan(batch, n_kv_heads, max_tiles, &a.n_splits, &a.tiles_per_split);
+    kvarn::decode_split_plan(batch, n_kv_heads, n_q_heads, max_tiles, &a.n_splits, &a.tiles_per_split);
     return hip_status(kvarn::launch_decode(a));
 }
 

@@ -45,9 +45,10 @@ struct DecodeArgs {
     hipStream_t stream;
 };
 
-// Split-K plan of the decode kernel: tiles of one (sequence, KV head) are cut
-// into n_splits ranges of tiles_per_split tiles.
-void decode_split_plan(int64_t batch, int n_kv_heads, int max_tiles, int* n_splits, int* tiles_per_split);
+// Split-K plan of the decode kernel: tiles of one (sequence, KV head, chunk of
+// 4 query heads) are cut into n_splits ranges of tiles_per_split tiles.
+void decode_split_plan(int64_t batch, int n_kv_heads, int n_q_heads, int max_tiles, int* n_splits,
+                       int* tiles_per_split);
 
 hipError_t launch_quantize(const QuantizeArgs& a);
 hipError_t launch_dequantize(const DequantizeArgs& a);

@@ -45,7 +45,8 @@
 //                     scale).  For V the last token step is skipped: its result
 //                     is absorbed into s1 and never stored.
 //   4. RTN + pack     code = clamp(rint((Zn - z) / s1), 0, L); each lane packs
-//                     its 8 codes of a token into 16 (2-bit) or 32 (4-bit) bits
+//                     8 codes of one code row (K: a token's 8 channels, V: a
+//                     channel's 8 tokens) into 16 (2-bit) or 32 (4-bit) bits
 //                     and stores them straight into the record.
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
@@ -528,29 +529,41 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
 
     // ---- 4. codes -------------------------------------------------------------------
     // t = (Zn - z) / s1 clamped to [0, L]; adding 2^23 rounds it to the nearest
-    // integer (ties to even) in the low mantissa bits.  The shifted sums of the
-    // 2^23 bit patterns are a constant, removed once per token.
+    // integer (ties to even) in the low mantissa bits.  Code rows follow the s2
+    // axis: K packs the 8 channels of each of the lane's tokens (token rows), V
+    // the 8 tokens of each of its channels (channel rows).  The shifted sums of
+    // the 2^23 bit patterns are a constant, removed once per packed word.
     constexpr uint32_t kBias = [] {
         uint32_t c = 0;
         for (int j = 0; j < 8; ++j) c += 0x4B000000u << (BITS * j);
         return c;
     }();
+    uint32_t word[8];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        uint32_t word = 0;
+    for (int k = 0; k < 8; ++k) word[k] = 0;
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int gi = (AXIS == kAxisK) ? j : a;
             float t = fmaf(y[a][j], inv_s1[gi], zoff[gi]);
             t = __builtin_amdgcn_fmed3f(t, 0.0f, kL) + kMagic;
-            word += __float_as_uint(t) << (BITS * j);
+            if constexpr (AXIS == kAxisK)
+                word[a] += __float_as_uint(t) << (BITS * j);
+            else
+                word[j] += __float_as_uint(t) << (BITS * a);
         }
-        word -= kBias;
-        uint8_t* dst = rec + (row0 + a) * R::kRowBytes;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        // K: row = token row0 + k, group offset = channel 8 * og; V: row = channel
+        // 8 * og + k, group offset = token row0
+        const int row = (AXIS == kAxisK) ? row0 + k : 8 * og + k;
+        const int g0 = (AXIS == kAxisK) ? 8 * og : row0;
+        uint8_t* dst = rec + row * R::kRowBytes + g0 * BITS / 8;
         if constexpr (BITS == 2)
-            *reinterpret_cast<uint16_t*>(dst + 2 * og) = (uint16_t)word;
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(word[k] - kBias);
         else
-            *reinterpret_cast<uint32_t*>(dst + 4 * og) = word;
+            *reinterpret_cast<uint32_t*>(dst) = word[k] - kBias;
     }
 }
 

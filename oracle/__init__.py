@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.kvo_codes_given_meta.restype = I
         L.kvo_codes_given_meta.argtypes = [P, I, I64, I64, I64, P, I, I, I, P, P, P]
         L.kvo_unpack_codes.restype = I
-        L.kvo_unpack_codes.argtypes = [P, I64, I, P]
+        L.kvo_unpack_codes.argtypes = [P, I64, I, I, P]
         L.kvo_dequantize_tiles.restype = I
         L.kvo_dequantize_tiles.argtypes = [P, I64, I, I, I, P]
         L.kvo_decode_attn.restype = I
@@ -191,11 +191,12 @@ def codes_given_meta(view: TileView, bits: int, axis: int, records: np.ndarray, 
     return codes, t
 
 
-def unpack_codes(records: np.ndarray, bits: int) -> np.ndarray:
+def unpack_codes(records: np.ndarray, bits: int, axis: int) -> np.ndarray:
+    """Codes of packed records as [n][128 tokens][128 channels] (code rows follow the s2 axis)."""
     records = np.ascontiguousarray(records, np.uint8).reshape(-1, record_bytes(bits))
     codes = np.empty((records.shape[0], N, N), np.uint8)
-    if lib().kvo_unpack_codes(_ptr(records), records.shape[0], bits, _ptr(codes)) != 0:
-        raise ValueError("bad bits")
+    if lib().kvo_unpack_codes(_ptr(records), records.shape[0], bits, axis, _ptr(codes)) != 0:
+        raise ValueError("bad bits or axis")
     return codes
 
 

@@ -45,9 +45,11 @@
  *              V  Yh_ij = s2_j * (code_ij * s1_i + z_i),   Xh = Yh * H.
  *
  * Packed record of one tile (bits b in {2, 4}), contiguous bytes:
- *   [0, 2048*b)            codes: token t occupies bytes [16*b*t, 16*b*(t+1));
- *                          channel c sits at byte 16*b*t + (c*b)/8, bit (c*b)%8,
- *                          least-significant bits first
+ *   [0, 2048*b)            codes, 128 rows of 16*b bytes.  Row r belongs to
+ *                          index r of the s2 axis (K: token r, V: channel r);
+ *                          within a row the code of group g (K: channel g,
+ *                          V: token g) sits at byte 16*b*r + (g*b)/8, bit
+ *                          (g*b)%8, least-significant bits first
  *   [2048*b, +128)         s1, FP8 E4M3, indexed by group
  *   [2048*b + 128, +128)   s2, FP8 E4M3, indexed by the other axis
  *   [2048*b + 256, +256)   z, FP16 little-endian, indexed by group
@@ -208,18 +210,23 @@ static size_t off_s1(int bits) { return (size_t)2048 * bits; }
 static size_t off_s2(int bits) { return (size_t)2048 * bits + 128; }
 static size_t off_z(int bits) { return (size_t)2048 * bits + 256; }
 
-static void put_code(uint8_t *rec, int bits, int t, int c, int code)
+/* Code of token t, channel c: row = s2 index, position in the row = group. */
+static size_t code_bit(int bits, int axis, int t, int c)
 {
-    size_t bit = (size_t)c * bits;
-    size_t byte = (size_t)16 * bits * t + bit / 8;
-    rec[byte] |= (uint8_t)(code << (bit % 8));
+    int row = axis == AX_K ? t : c, g = axis == AX_K ? c : t;
+    return (size_t)16 * bits * 8 * row + (size_t)g * bits;
 }
 
-static int get_code(const uint8_t *rec, int bits, int t, int c)
+static void put_code(uint8_t *rec, int bits, int axis, int t, int c, int code)
 {
-    size_t bit = (size_t)c * bits;
-    size_t byte = (size_t)16 * bits * t + bit / 8;
-    return (rec[byte] >> (bit % 8)) & ((1 << bits) - 1);
+    size_t bit = code_bit(bits, axis, t, c);
+    rec[bit / 8] |= (uint8_t)(code << (bit % 8));
+}
+
+static int get_code(const uint8_t *rec, int bits, int axis, int t, int c)
+{
+    size_t bit = code_bit(bits, axis, t, c);
+    return (rec[bit / 8] >> (bit % 8)) & ((1 << bits) - 1);
 }
 
 static double rec_s1(const uint8_t *rec, int bits, int g) { return kvo_fp8_decode(rec[off_s1(bits) + g]); }
@@ -456,7 +463,7 @@ static void quantize_one(const double *y, int bits, int axis, int n_iter, uint8_
         for (int j = 0; j < N; ++j) {
             int gi = grp(axis, i, j);
             double zn = y[i * N + j] / s2[sidx(axis, i, j)];
-            put_code(rec, bits, i, j, rtn_code(zn, z[gi], s1[gi], bits, NULL));
+            put_code(rec, bits, axis, i, j, rtn_code(zn, z[gi], s1[gi], bits, NULL));
         }
     write_meta(rec, bits, s1, s2, z);
     if (g_pre_out)
@@ -561,16 +568,16 @@ int kvo_codes_given_meta(const void *x, int dtype, int64_t n_tiles, int64_t tile
     return 0;
 }
 
-/* Codes of packed records, unpacked to one byte per element [n][128][128]. */
-int kvo_unpack_codes(const uint8_t *records, int64_t n_tiles, int bits, uint8_t *codes)
+/* Codes of packed records, unpacked to one byte per element [n][128 tokens][128 channels]. */
+int kvo_unpack_codes(const uint8_t *records, int64_t n_tiles, int bits, int axis, uint8_t *codes)
 {
-    if (!(bits == 2 || bits == 4) || n_tiles < 0)
+    if (!(bits == 2 || bits == 4) || !(axis == AX_K || axis == AX_V) || n_tiles < 0)
         return -1;
     size_t pb = kvo_record_bytes(bits);
     for (int64_t n = 0; n < n_tiles; ++n)
         for (int i = 0; i < N; ++i)
             for (int j = 0; j < N; ++j)
-                codes[n * NN + i * N + j] = (uint8_t)get_code(records + n * pb, bits, i, j);
+                codes[n * NN + i * N + j] = (uint8_t)get_code(records + n * pb, bits, axis, i, j);
     return 0;
 }
 
@@ -586,7 +593,7 @@ static void dequant_one(const uint8_t *rec, int bits, int axis, int rotate, cons
         for (int j = 0; j < N; ++j) {
             int gi = grp(axis, i, j);
             yh[i * N + j] = rec_s2(rec, bits, sidx(axis, i, j)) *
-                            (get_code(rec, bits, i, j) * rec_s1(rec, bits, gi) + rec_z(rec, bits, gi));
+                            (get_code(rec, bits, axis, i, j) * rec_s1(rec, bits, gi) + rec_z(rec, bits, gi));
         }
     if (rotate)
         rotate_rows(yh, out, h); /* H is symmetric and orthogonal: its own inverse */

@@ -103,7 +103,7 @@ def compare_quantize(view: "oracle.TileView", bits: int, axis: int, gpu_rec: np.
 
     # 3. codes, given all of the GPU's metadata
     codes_ref, t = oracle.codes_given_meta(view, bits, axis, gpu_rec)
-    codes_gpu = oracle.unpack_codes(gpu_rec, bits)
+    codes_gpu = oracle.unpack_codes(gpu_rec, bits, axis)
     diff = codes_gpu.astype(np.int64) - codes_ref.astype(np.int64)
     s1g = s1_gpu[:, None, :] if axis == 0 else s1_gpu[:, :, None]
     zg = z_gpu[:, None, :] if axis == 0 else z_gpu[:, :, None]
@@ -113,7 +113,7 @@ def compare_quantize(view: "oracle.TileView", bits: int, axis: int, gpu_rec: np.
     rep["code_bad"] = int(((diff != 0) & ~((np.abs(diff) == 1) & tie)).sum())
 
     # 4. raw agreement of the packed records
-    raw_codes = oracle.unpack_codes(ref_rec, bits)
+    raw_codes = oracle.unpack_codes(ref_rec, bits, axis)
     rep["raw_identical_codes"] = float((raw_codes == codes_gpu).mean())
     rep["records_identical"] = int((gpu_rec == ref_rec).all(1).sum())
     rep["unexplained"] = rep["s2_bad"] + rep["s1_bad"] + rep["z_bad"] + rep["code_bad"]

@@ -25,8 +25,9 @@ def test_single_code_closed_form(orc, axis, bits):
     """One non-zero code: the dequantised tile is s2*code*s1 times one row of H."""
     rec = _blank_record(orc, bits)
     t0, c0, code = 37, 90, 2 ** bits - 1
-    byte = 16 * bits * t0 + (c0 * bits) // 8
-    rec[0, byte] |= code << ((c0 * bits) % 8)
+    row, g = (t0, c0) if axis == K else (c0, t0)  # code rows follow the s2 axis
+    byte = 16 * bits * row + (g * bits) // 8
+    rec[0, byte] |= code << ((g * bits) % 8)
     base = 2048 * bits
     g1, g2 = (c0, t0) if axis == K else (t0, c0)
     rec[0, base + g1] = 0x3C       # s1 = 1.5

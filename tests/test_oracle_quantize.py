@@ -120,7 +120,7 @@ def test_codes_are_brute_force_nearest_levels(orc, tiny_tiles, axis, bits):
     tiles = tiny_tiles[axis][:4]
     view = orc.TileView.dense(tiles, orc.DT_F16)
     rec, dbg = orc.quantize(view, bits, axis, debug=True)
-    codes = orc.unpack_codes(rec, bits).astype(np.int64)
+    codes = orc.unpack_codes(rec, bits, axis).astype(np.int64)
     _, s1b, s2b, zb = orc.record_fields(rec, bits)
     import torch
 
@@ -207,7 +207,7 @@ def test_kivi_special_case_exact(orc, axis, bits):
     assert np.array_equal(xf.astype(np.float64), x)
     view = orc.TileView.dense(xf, orc.DT_F32)
     rec = orc.quantize(view, bits, axis, n_iter=0, rotate=False)
-    codes = orc.unpack_codes(rec, bits)
+    codes = orc.unpack_codes(rec, bits, axis)
     assert np.array_equal(codes, k)
     _, s1b, s2b, zb = orc.record_fields(rec, bits)
     assert np.all(s2b == 0x30)  # FP8 0.5
@@ -228,7 +228,7 @@ def test_rotation_only_special_case(orc, axis):
     x = (g @ hadamard_ref()).astype(np.float32)
     view = orc.TileView.dense(x, orc.DT_F32)
     rec = orc.quantize(view, bits, axis, n_iter=0, rotate=True)
-    assert np.array_equal(orc.unpack_codes(rec, bits), k)
+    assert np.array_equal(orc.unpack_codes(rec, bits, axis), k)
     back = orc.dequantize(rec, bits, axis, rotate=True)
     assert np.abs(back - x).max() < 1e-5 * np.abs(x).max()
 
@@ -253,16 +253,19 @@ def test_power_of_two_input_scaling(orc, tiny_tiles, axis, shift):
     assert np.array_equal(z1.view(np.float16).astype(np.float64), z0.view(np.float16).astype(np.float64) * 2.0 ** shift)
 
 
-def test_packing_layout(orc):
-    """Codes are token-major rows of 16*b bytes, channel c at bit c*b, LSB first."""
-    rng = np.random.default_rng(30)
+@pytest.mark.parametrize("axis", [K, V])
+def test_packing_layout(orc, axis):
+    """Codes are rows of 16*b bytes along the s2 axis (K: token rows, V: channel
+    rows); the code of group g sits at bit g*b of its row, LSB first."""
+    rng = np.random.default_rng(30 + axis)
     for bits in (2, 4):
-        k, d, m, x = _grid_tile(rng, K, bits, 1)
-        rec = orc.quantize(orc.TileView.dense(x.astype(np.float32), orc.DT_F32), bits, K, n_iter=0,
+        k, d, m, x = _grid_tile(rng, axis, bits, 1)
+        rec = orc.quantize(orc.TileView.dense(x.astype(np.float32), orc.DT_F32), bits, axis, n_iter=0,
                            rotate=False)[0]
         for t, c in [(0, 0), (0, 1), (5, 3), (17, 64), (127, 127), (64, 126)]:
-            byte = rec[16 * bits * t + (c * bits) // 8]
-            assert (byte >> ((c * bits) % 8)) & (2 ** bits - 1) == k[0, t, c]
+            row, g = (t, c) if axis == K else (c, t)
+            byte = rec[16 * bits * row + (g * bits) // 8]
+            assert (byte >> ((g * bits) % 8)) & (2 ** bits - 1) == k[0, t, c]
 
 
 def test_constant_tile_reconstructs(orc):
