@@ -24,14 +24,21 @@
  *    quantised when it fills (pheeree.github.io blog, part 3; dimensionstp
  *    review, section 3-2(1): one 128-token block is one tile).
  *  - Packed record of one tile, kvarn_tile_bytes(bits) bytes, 16-byte aligned:
- *      [0, 2048*b)          codes, 128 rows of 16*b bytes.  Row r belongs to
- *                           index r of the s2 axis: token r for K, channel r
- *                           for V.  Within row r the code of group g (K:
- *                           channel g, V: token g) is at byte 16*b*r + g*b/8,
- *                           bit (g*b)%8, least significant first.  (Each
- *                           reader then finds the 32 codes of one row that a
- *                           decode contraction needs in 8 contiguous bytes:
- *                           a token's channels for K, a channel's tokens for V.)
+ *      [0, 2048*b)          codes.  Row r is index r of the s2 axis (token r
+ *                           for K, channel r for V); position p is the group
+ *                           index (channel p for K, token p for V).  With
+ *                           n = r/8 and i = r%8 the code of (r, p) is at
+ *                             b = 2: byte 1024*(i/2) + 16*(16*(p/32) + n)
+ *                                         + 8*(i%2) + (p%32)/4, bit 2*(p%4)
+ *                             b = 4: byte 1024*i + 16*(16*((p/16)%4) + n)
+ *                                         + 8*(p/64) + (p%16)/2, bit 4*(p%2)
+ *                           least significant bits first.  This is the order
+ *                           in which decode attention feeds the codes to the
+ *                           matrix cores: lane 16g + n of a wave reads one
+ *                           16-byte chunk per 1 KiB block, so every load of
+ *                           the wave is 1 KiB contiguous.  The 8 codes of one
+ *                           row at positions 8j..8j+7 are always one 2-byte
+ *                           (b = 2) or 4-byte (b = 4) unit.
  *      [2048*b, +128)       s1, FP8 E4M3 (OCP), one per group
  *      [2048*b + 128, +128) s2, FP8 E4M3, one per index of the other axis
  *      [2048*b + 256, +256) z, IEEE FP16 little-endian, one per group
@@ -63,7 +70,7 @@ extern "C" {
 
 #define KVARN_HEAD_DIM 128
 #define KVARN_TILE_TOKENS 128
-#define KVARN_FORMAT_VERSION 2
+#define KVARN_FORMAT_VERSION 3
 
 /* Status codes returned by the entry points. */
 enum {

@@ -113,18 +113,21 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Load the 32 codes of record row `row` that lane group gl feeds (8 bytes for
-// 2 bits, two times 8 bytes for 4 bits).
+// Codes of record rows 8n + blk (blk = 0..7) that lane 16 gl + n feeds: in the
+// record's operand order they are 4 (2-bit) or 8 (4-bit) 16-byte chunks at
+// 1 KiB strides, each instruction reading 1 KiB contiguous over the wave.
 template <int BITS>
-__device__ __forceinline__ uint4 load_row_codes(__amdgpu_buffer_rsrc_t r, int row, int gl) {
-    using R = Rec<BITS>;
-    const int p = row * R::kRowBytes + 8 * gl;
+__device__ __forceinline__ void load_codes(__amdgpu_buffer_rsrc_t r, int lane, uint4 (&c)[8]) {
     if constexpr (BITS == 2) {
-        const uint2 a = ld8(r, p);
-        return make_uint4(a.x, a.y, 0u, 0u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = ld16(r, 1024 * i + 16 * lane);
+            c[2 * i] = make_uint4(v.x, v.y, 0u, 0u);        // row 8n + 2i
+            c[2 * i + 1] = make_uint4(v.z, v.w, 0u, 0u);    // row 8n + 2i + 1
+        }
     } else {
-        const uint2 a = ld8(r, p), b = ld8(r, p + 32);
-        return make_uint4(a.x, a.y, b.x, b.y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = ld16(r, 1024 * i + 16 * lane);
     }
 }
 
@@ -307,10 +310,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         const bool ok = idx >= 0;
         const __amdgpu_buffer_rsrc_t rk = record_rsrc(kp + (ok ? idx : 0) * RK::kBytes, ok ? RK::kBytes : 0);
         const __amdgpu_buffer_rsrc_t rv = record_rsrc(vp + (ok ? idx : 0) * RV::kBytes, ok ? RV::kBytes : 0);
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) t.kc[blk] = load_row_codes<BK>(rk, 8 * n + blk, gl);
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) t.vc[blk] = load_row_codes<BV>(rv, 8 * n + blk, gl);
+        load_codes<BK>(rk, lane, t.kc);
+        load_codes<BV>(rv, lane, t.vc);
         t.ks1 = ld8(rk, RK::kS1 + 8 * G);
         t.kz = ld16(rk, RK::kZ + 16 * G);
         t.ks2 = ld8(rk, RK::kS2 + 8 * n);

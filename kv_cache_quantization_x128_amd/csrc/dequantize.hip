@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
     for (int i = 0; i < 8; ++i) {
         const int row = (AXIS == kAxisK) ? row0 + i : 8 * cg + i;
         const int g0 = (AXIS == kAxisK) ? 8 * cg : row0;
-        const uint8_t* p = rec + row * R::kRowBytes + g0 * BITS / 8;
+        const uint8_t* p = rec + R::piece(row, g0);
         wd[i] = (BITS == 2) ? (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p))
                             : __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
     }

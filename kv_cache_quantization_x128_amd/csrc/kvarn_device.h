@@ -20,13 +20,27 @@ enum : int { kAxisK = 0, kAxisV = 1 };
 
 template <int BITS>
 struct Rec {
-    static constexpr int kCodeBytes = 2048 * BITS;   // 128 tokens x 16*BITS bytes
-    static constexpr int kRowBytes = 16 * BITS;      // codes of one token
+    static constexpr int kCodeBytes = 2048 * BITS;   // 128 rows x 128 codes
     static constexpr int kS1 = kCodeBytes;           // FP8 group scales
     static constexpr int kS2 = kCodeBytes + 128;     // FP8 second scales
     static constexpr int kZ = kCodeBytes + 256;      // FP16 zero-points
     static constexpr int kBytes = kCodeBytes + 512;
     static constexpr int kL = (1 << BITS) - 1;
+
+    // Byte offset of the 8 codes of row r (s2 index) at positions p0..p0+7
+    // (group indices, p0 a multiple of 8), packed LSB first: 2 bytes for 2-bit
+    // codes, 4 for 4-bit.  The code block is ordered as the decode kernel's
+    // matrix-core operands consume it (see include/kvarn.h): with n = r/8,
+    // i = r%8, the 32 (2-bit) or 2 x 16 (4-bit) codes that lane 16g + n feeds
+    // for row 8n + i are one 8- or 16-byte chunk, and the chunks of all 64
+    // lanes for one i (4-bit) or one pair of i (2-bit) are 1 KiB contiguous.
+    static __device__ __forceinline__ int piece(int r, int p0) {
+        const int n = r >> 3, i = r & 7;
+        if constexpr (BITS == 2)
+            return 1024 * (i >> 1) + 16 * (16 * (p0 >> 5) + n) + 8 * (i & 1) + ((p0 & 31) >> 2);
+        else
+            return 1024 * i + 16 * (16 * ((p0 >> 4) & 3) + n) + 8 * (p0 >> 6) + ((p0 & 15) >> 1);
+    }
 };
 
 // ---------------------------------------------------------------- conversions

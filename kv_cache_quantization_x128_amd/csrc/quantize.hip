@@ -559,7 +559,7 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
         // 8 * og + k, group offset = token row0
         const int row = (AXIS == kAxisK) ? row0 + k : 8 * og + k;
         const int g0 = (AXIS == kAxisK) ? 8 * og : row0;
-        uint8_t* dst = rec + row * R::kRowBytes + g0 * BITS / 8;
+        uint8_t* dst = rec + R::piece(row, g0);
         if constexpr (BITS == 2)
             *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(word[k] - kBias);
         else

@@ -45,11 +45,17 @@
  *              V  Yh_ij = s2_j * (code_ij * s1_i + z_i),   Xh = Yh * H.
  *
  * Packed record of one tile (bits b in {2, 4}), contiguous bytes:
- *   [0, 2048*b)            codes, 128 rows of 16*b bytes.  Row r belongs to
- *                          index r of the s2 axis (K: token r, V: channel r);
- *                          within a row the code of group g (K: channel g,
- *                          V: token g) sits at byte 16*b*r + (g*b)/8, bit
- *                          (g*b)%8, least-significant bits first
+ *   [0, 2048*b)            codes.  Row r is index r of the s2 axis (K: token r,
+ *                          V: channel r), position p its group index (K:
+ *                          channel p, V: token p).  With n = r/8, i = r%8 the
+ *                          code sits at
+ *                            b = 2: byte 1024*(i/2) + 16*(16*(p/32) + n)
+ *                                        + 8*(i%2) + (p%32)/4,  bit 2*(p%4)
+ *                            b = 4: byte 1024*i + 16*(16*((p/16)%4) + n)
+ *                                        + 8*(p/64) + (p%16)/2, bit 4*(p%2)
+ *                          (the order in which the decode kernel's matrix
+ *                          instructions consume them; a reading of the pages,
+ *                          which fix only the bit count)
  *   [2048*b, +128)         s1, FP8 E4M3, indexed by group
  *   [2048*b + 128, +128)   s2, FP8 E4M3, indexed by the other axis
  *   [2048*b + 256, +256)   z, FP16 little-endian, indexed by group
@@ -210,11 +216,17 @@ static size_t off_s1(int bits) { return (size_t)2048 * bits; }
 static size_t off_s2(int bits) { return (size_t)2048 * bits + 128; }
 static size_t off_z(int bits) { return (size_t)2048 * bits + 256; }
 
-/* Code of token t, channel c: row = s2 index, position in the row = group. */
+/* Bit offset of the code of token t, channel c (layout in the header above). */
 static size_t code_bit(int bits, int axis, int t, int c)
 {
-    int row = axis == AX_K ? t : c, g = axis == AX_K ? c : t;
-    return (size_t)16 * bits * 8 * row + (size_t)g * bits;
+    int r = axis == AX_K ? t : c, p = axis == AX_K ? c : t;
+    int n = r / 8, i = r % 8;
+    size_t byte;
+    if (bits == 2)
+        byte = (size_t)1024 * (i / 2) + 16 * (16 * (p / 32) + n) + 8 * (i % 2) + (p % 32) / 4;
+    else
+        byte = (size_t)1024 * i + 16 * (16 * ((p / 16) % 4) + n) + 8 * (p / 64) + (p % 16) / 2;
+    return 8 * byte + (size_t)(bits == 2 ? 2 * (p % 4) : 4 * (p % 2));
 }
 
 static void put_code(uint8_t *rec, int bits, int axis, int t, int c, int code)

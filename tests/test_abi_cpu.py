@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_host_helpers():
-    assert kvarn.format_version() == 2
+    assert kvarn.format_version() == 3
     assert kvarn.tile_bytes(2) == 4608 and kvarn.tile_bytes(4) == 8704 and kvarn.tile_bytes(3) == 0
     assert kvarn.parse_preset("kvarn_k4v2_g128") == (4, 2, 128)
     assert kvarn.parse_preset("kvarn_k2v2_g128") == (2, 2, 128)

@@ -255,17 +255,25 @@ def test_power_of_two_input_scaling(orc, tiny_tiles, axis, shift):
 
 @pytest.mark.parametrize("axis", [K, V])
 def test_packing_layout(orc, axis):
-    """Codes are rows of 16*b bytes along the s2 axis (K: token rows, V: channel
-    rows); the code of group g sits at bit g*b of its row, LSB first."""
+    """Codes sit where include/kvarn.h documents them (rows along the s2 axis,
+    chunks in the decode operand order), and every code bit of the block is
+    used exactly once."""
+    from test_oracle_dequant_decode import code_position
+
     rng = np.random.default_rng(30 + axis)
     for bits in (2, 4):
         k, d, m, x = _grid_tile(rng, axis, bits, 1)
         rec = orc.quantize(orc.TileView.dense(x.astype(np.float32), orc.DT_F32), bits, axis, n_iter=0,
                            rotate=False)[0]
-        for t, c in [(0, 0), (0, 1), (5, 3), (17, 64), (127, 127), (64, 126)]:
-            row, g = (t, c) if axis == K else (c, t)
-            byte = rec[16 * bits * row + (g * bits) // 8]
-            assert (byte >> ((g * bits) % 8)) & (2 ** bits - 1) == k[0, t, c]
+        for t, c in [(0, 0), (0, 1), (5, 3), (17, 64), (127, 127), (64, 126), (9, 33), (100, 71)]:
+            byte, bit = code_position(bits, axis, t, c)
+            assert (rec[byte] >> bit) & (2 ** bits - 1) == k[0, t, c]
+        seen = np.zeros(2048 * bits * 8, np.int64)
+        for t in range(128):
+            for c in range(128):
+                byte, bit = code_position(bits, axis, t, c)
+                seen[8 * byte + bit: 8 * byte + bit + bits] += 1
+        assert (seen == 1).all()
 
 
 def test_constant_tile_reconstructs(orc):
