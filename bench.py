@@ -7,8 +7,10 @@ tiles and 18432 V tiles, 2-bit.  Inputs are resident in HBM before timing.
 
 value = fp16-equivalent bytes moved by the step (36864 tiles x 32 KiB in the
 quantiser + the same out of the dequantiser) / step time.  The roofline object
-describes the dominant kernel (the quantiser): its algorithmic bytes per launch
-(tiles x (32768 + 4608)) over its HIP-event-timed average launch duration.
+describes the dominant kernel (the quantiser), which is bound by fp32 vector
+arithmetic: its algorithmic flops per launch (quantize_flops_per_tile) over its
+HIP-event-timed average launch duration, against the fp32 vector peak; its
+algorithmic HBM rate (tiles x (32768 + 4608) bytes) is reported beside it.
 Decode attention over the 2-bit cache (batch 16, 32 query heads on 8 KV heads,
 32768 tokens, 36 layers) is timed in the same run and reported in its own object.
 The oracle's quantise + dequantise is timed on a bounded sample on the host.
@@ -30,11 +32,25 @@ sys.path.insert(0, ROOT)
 from kv_cache_quantization_x128_amd import kvarn, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak (counts packed FP32 FMA)
 TILE_F16_BYTES = 128 * 128 * 2
+
+
+def quantize_flops_per_tile(axis, n_iter=8):
+    """Algorithmic fp32 operations of quantising one 128 x 128 tile.
+
+    per element: rotation 7 butterfly add/sub + 1 scale = 8; each normalisation
+    half-step 1 multiply by the factor + 1 add (sum) + 1 FMA (sum of squares, 2) = 4,
+    2 * n_iter half-steps for K, 2 * n_iter - 1 for V (the last token factor of V
+    is absorbed into s1 and never needed); metadata and codes: Zn multiply 1, group
+    min and max 2, (Zn - z) / s1 as one FMA 2 = 5.
+    """
+    half_steps = 2 * n_iter - (1 if axis == kvarn.AXIS_V and n_iter > 0 else 0)
+    return 128 * 128 * (8 + 4 * half_steps + 5)
 CSRC = os.path.join(ROOT, "kv_cache_quantization_x128_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_decode_append.json")
 KERNEL_SOURCES = {"quantize": ("quantize.hip", "kvarn_device.h"), "dequantize": ("dequantize.hip", "kvarn_device.h"),
-                  "decode_partial": ("decode_attn.hip", "kvarn_device.h")}
+                  "decode_mfma": ("decode_attn.hip", "kvarn_device.h")}
 
 
 def log(*a):
@@ -165,7 +181,7 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
         "wall_s_per_pass": wall / passes,
         "fp16_equiv_GBs": 2 * batch * hkv * nt * TILE_F16_BYTES / (layer_ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode_partial"),
+                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode_mfma"),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "tokens_per_s": batch * hq / (layer_ms * 1e-3),
     }
@@ -248,9 +264,14 @@ def main():
     q_alg = n * (TILE_F16_BYTES + pb)
     q_ach = q_alg / (q_ms * 1e-3) / 1e9
     dq_ach = q_alg / (dq_ms * 1e-3) / 1e9
+    # the quantiser is bound by fp32 vector arithmetic (the normalisation sweeps),
+    # not by HBM: its roofline is algorithmic flops per launch over launch time
+    q_flops = n * 0.5 * (quantize_flops_per_tile(kvarn.AXIS_K) + quantize_flops_per_tile(kvarn.AXIS_V))
+    q_tflops = q_flops / (q_ms * 1e-3) / 1e12
     ops = {
         "quantize": {"launch_ms": q_ms, "tiles_per_launch": n, "tiles_per_s": n / (q_ms * 1e-3),
                      "algorithmic_GBs": q_ach, "frac_hbm": q_ach / HBM_PEAK_GBS,
+                     "algorithmic_TFLOPs": q_tflops, "frac_fp32_vector_peak": q_tflops / FP32_VECTOR_PEAK_TFLOPS,
                      "fp16_equiv_GBs": n * TILE_F16_BYTES / (q_ms * 1e-3) / 1e9},
         "dequantize": {"launch_ms": dq_ms, "tiles_per_launch": n, "tiles_per_s": n / (dq_ms * 1e-3),
                        "algorithmic_GBs": dq_ach, "frac_hbm": dq_ach / HBM_PEAK_GBS,
@@ -274,9 +295,10 @@ def main():
                                "128-token block each, head_dim 128, bf16 K and V, 2-bit",
                    "tiles_per_step": 2 * n, "layout": "[layer][seq][token][head][128]", "n_iter": 8},
         "frac_of_hbm_peak": value / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": q_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": q_ach / HBM_PEAK_GBS, "traffic": measured_traffic("quantize"),
-                     "algorithmic_bytes_per_launch": q_alg},
+        "roofline": {"bound": "alu", "kernel": "quantize_kernel", "achieved": q_tflops,
+                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": q_tflops / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": measured_traffic("quantize"), "algorithmic_flops_per_launch": q_flops,
+                     "algorithmic_bytes_per_launch": q_alg, "hbm_GBs": q_ach, "hbm_frac": q_ach / HBM_PEAK_GBS},
         "ops": ops,
     }
     if not args.no_decode:

@@ -34,7 +34,8 @@ namespace kvarn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPart = 2 + kN;  // m (log2 domain), l, acc[128] per (sequence, query head, split)
+constexpr int kPart = kDecodePart;  // m (log2 domain), l, 6 unused, acc[128] per (sequence, query head, split)
+constexpr int kAcc = 8;             // float offset of acc[] in a partial (16-byte aligned)
 constexpr int kPiecesQ = 4;   // query pieces: score error ~2^-17 relative per product
 constexpr int kPiecesP = 3;   // weight pieces
 
@@ -177,8 +178,8 @@ __device__ __forceinline__ void write_pieces(uint8_t* __restrict__ stage, int of
         e = __builtin_amdgcn_cvt_pk_fp8_f32(u[4], u[6], e, true);
         o = __builtin_amdgcn_cvt_pk_fp8_f32(u[1], u[3], o, false);
         o = __builtin_amdgcn_cvt_pk_fp8_f32(u[5], u[7], o, true);
-        *reinterpret_cast<int*>(stage + off_e + 32 * k) = e;
-        *reinterpret_cast<int*>(stage + off_o + 32 * k) = o;
+        *reinterpret_cast<int*>(stage + off_e + 48 * k) = e;
+        *reinterpret_cast<int*>(stage + off_o + 48 * k) = o;
         if (k + 1 < PIECES) {
             f2 b;
             b = __builtin_amdgcn_cvt_pk_f32_fp8(e, false); u[0] = 16.0f * (u[0] - b.x), u[2] = 16.0f * (u[2] - b.y);
@@ -189,25 +190,32 @@ __device__ __forceinline__ void write_pieces(uint8_t* __restrict__ stage, int of
     }
 }
 
+// A staging buffer: the 32 bytes of operand lane A sit at stage_lane(A); the
+// 48-byte pitch plus a 16-byte shift per lane group spreads both the dword
+// writes of the piece writers and the 16-byte reads of the operand lanes over
+// the LDS banks (at most 4-way conflicts on 32 banks, 2-way on 64).
+constexpr int kStageBytes = 48 * 64 + 16 * 3 + 16;
+__device__ __forceinline__ int stage_lane(int a) { return 48 * a + 16 * ((a >> 4) & 3); }
+
 // Byte offsets in the A staging buffer of the piece-0 dwords of positions
-// {x0, x0+2, x0+4, x0+6} (x0 = 8J or 8J+1) for query qg.
+// {x0, x0+2, x0+4, x0+6} (x0 = 8J or 8J+1) for query qg; piece k is 48k further.
 template <int BITS>
 __device__ __forceinline__ int piece_offset(int x0, int qg) {
     int gl, s;
     fp8_slot(kpos<BITS>(x0), gl, s);
-    return (16 * gl + 4 * qg) * 32 + s;
+    return stage_lane(16 * gl + 4 * qg) + s;
 }
 
-// Raw bytes of one K/V tile pair as one lane needs them.
+// Raw bytes of one K/V tile pair as one lane loads them.
 struct TileRaw {
     uint4 kc[8], vc[8];          // codes of record rows 8n + blk (lane group's 8 or 16 bytes)
-    uint2 ks1, ks2, vs1, vs2;    // FP8 scales: K s1 of channels 8G.., K s2 / V s1 of tokens 8n.., V s2 of channels 8n..
-    uint4 kz, vz;                // FP16 zero-points: K of channels 8G.., V of tokens 8n..
+    uint2 km, vm;                // bytes 8*lane.. of the 512-byte metadata blocks (s1, s2, z)
 };
 
 struct WaveSmem {
-    uint8_t qa[64 * 32];   // A operand staging: query pieces (scores)
-    uint8_t pa[64 * 32];   // A operand staging: weight pieces (values)
+    uint8_t qa[kStageBytes];     // A operand staging: query pieces (scores)
+    uint8_t pa[kStageBytes];     // A operand staging: weight pieces (values)
+    uint2 kmeta[64], vmeta[64];  // metadata blocks of the tile pair being computed
 };
 
 template <int BK, int BV>
@@ -280,10 +288,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const int qoff_e = piece_offset<BK>(8 * G, qg), qoff_o = piece_offset<BK>(8 * G + 1, qg);
     const int poff_e = piece_offset<BV>(8 * n, qg), poff_o = piece_offset<BV>(8 * n + 1, qg);
     // rows of unused pieces (piece 3 of the weights) stay zero
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        reinterpret_cast<int*>(sm.qa)[lane * 8 + i] = 0;
-        reinterpret_cast<int*>(sm.pa)[lane * 8 + i] = 0;
+    for (int i = lane; i < kStageBytes / 4; i += 64) {
+        reinterpret_cast<int*>(sm.qa)[i] = 0;
+        reinterpret_cast<int*>(sm.pa)[i] = 0;
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -295,7 +302,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     nt = nt < 0 ? 0 : (nt > max_tiles ? max_tiles : nt);
     const int j0 = split * tiles_per_split;
     const int j1 = min(j0 + tiles_per_split, nt);
-    const int gl = lane >> 4;                            // lane group of the B operand
     const int64_t row_base = ((int64_t)b * n_kv_heads + kvh) * max_tiles;
     const float e2 = pow2f((int)qexp);                  // 2^exponent of the query scaling
 
@@ -312,20 +318,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         const __amdgpu_buffer_rsrc_t rv = record_rsrc(vp + (ok ? idx : 0) * RV::kBytes, ok ? RV::kBytes : 0);
         load_codes<BK>(rk, lane, t.kc);
         load_codes<BV>(rv, lane, t.vc);
-        t.ks1 = ld8(rk, RK::kS1 + 8 * G);
-        t.kz = ld16(rk, RK::kZ + 16 * G);
-        t.ks2 = ld8(rk, RK::kS2 + 8 * n);
-        t.vs1 = ld8(rv, RV::kS1 + 8 * n);
-        t.vz = ld16(rv, RV::kZ + 16 * n);
-        t.vs2 = ld8(rv, RV::kS2 + 8 * n);
+        t.km = ld8(rk, RK::kS1 + 8 * lane);
+        t.vm = ld8(rv, RV::kS1 + 8 * lane);
     };
     auto compute = [&](const TileRaw& t) {
+        // ---- metadata through LDS: each lane picks the scales of its channels / tokens
+        sm.kmeta[lane] = t.km;
+        sm.vmeta[lane] = t.vm;
+        __builtin_amdgcn_wave_barrier();
+        const uint8_t* km = reinterpret_cast<const uint8_t*>(sm.kmeta);
+        const uint8_t* vm = reinterpret_cast<const uint8_t*>(sm.vmeta);
         // ---- query pieces q~_c s1_c (channels 8G..8G+7 of query qg) and z term
         float cz;
         {
             float s1[8], z[8], u[8];
-            fp8x8(t.ks1, s1);
-            f16x8(t.kz, z);
+            fp8x8(*reinterpret_cast<const uint2*>(km + 8 * G), s1);
+            f16x8(*reinterpret_cast<const uint4*>(km + 256 + 16 * G), z);
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) u[i] = qh[i] * s1[i], part = fmaf(qh[i], z[i], part);
@@ -335,15 +343,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         __builtin_amdgcn_wave_barrier();
         v8i aq;
         {
-            const int4 x0 = *reinterpret_cast<const int4*>(sm.qa + 32 * lane);
-            const int4 x1 = *reinterpret_cast<const int4*>(sm.qa + 32 * lane + 16);
+            const int4 x0 = *reinterpret_cast<const int4*>(sm.qa + stage_lane(lane));
+            const int4 x1 = *reinterpret_cast<const int4*>(sm.qa + stage_lane(lane) + 16);
             aq[0] = x0.x, aq[1] = x0.y, aq[2] = x0.z, aq[3] = x0.w, aq[4] = x1.x, aq[5] = x1.y, aq[6] = x1.z, aq[7] = x1.w;
         }
         // ---- scores of tokens 8n + blk for query qg
         float sc[8];
         {
             float s2[8];
-            fp8x8(t.ks2, s2);
+            fp8x8(*reinterpret_cast<const uint2*>(km + 128 + 8 * n), s2);
             v4f d[8];   // eight independent products, issued back to back
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
@@ -375,8 +383,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         float zs;
         {
             float s1[8], z[8], u[8];
-            fp8x8(t.vs1, s1);
-            f16x8(t.vz, z);
+            fp8x8(*reinterpret_cast<const uint2*>(vm + 8 * n), s1);
+            f16x8(*reinterpret_cast<const uint4*>(vm + 256 + 16 * n), z);
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) u[i] = p[i] * s1[i], part = fmaf(p[i], z[i], part);
@@ -386,14 +394,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         __builtin_amdgcn_wave_barrier();
         v8i ap;
         {
-            const int4 x0 = *reinterpret_cast<const int4*>(sm.pa + 32 * lane);
-            const int4 x1 = *reinterpret_cast<const int4*>(sm.pa + 32 * lane + 16);
+            const int4 x0 = *reinterpret_cast<const int4*>(sm.pa + stage_lane(lane));
+            const int4 x1 = *reinterpret_cast<const int4*>(sm.pa + stage_lane(lane) + 16);
             ap[0] = x0.x, ap[1] = x0.y, ap[2] = x0.z, ap[3] = x0.w, ap[4] = x1.x, ap[5] = x1.y, ap[6] = x1.z, ap[7] = x1.w;
         }
         // ---- values: channels 8n + blk for query qg
         {
             float s2[8];
-            fp8x8(t.vs2, s2);
+            fp8x8(*reinterpret_cast<const uint2*>(vm + 128 + 8 * n), s2);
             v4f d[8];
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
@@ -429,41 +437,80 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     if (q_ok) {
         float* dst = ws + ((b * n_q_heads + hq) * n_splits + split) * kPart;
         if (n == 0) dst[0] = m_run, dst[1] = l_run;
-        float* a = dst + 2 + 8 * n;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = acc[i];
+        float4* a = reinterpret_cast<float4*>(dst + kAcc + 8 * n);
+        a[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        a[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
 }
 
-// One workgroup of 128 threads per (sequence, query head): log-sum-exp merge of
-// the splits, inverse rotation, FP16.
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws, int n_splits,
-                                                             uint16_t* __restrict__ out) {
-    __shared__ float sO[kN];
-    const int64_t row = blockIdx.x;  // b * n_q_heads + hq
-    const int d = threadIdx.x;
-    const float* p = ws + row * n_splits * kPart;
+// One wave per (sequence, KV head, chunk of 4 query heads): log-sum-exp merge
+// of the splits, inverse rotation (the same 16-lane Hadamard network as the
+// query rotation), FP16.  Lane = (query qg, channels 8n..8n+7).
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws, int n_splits,
+                                                            int n_q_heads, int n_kv_heads, int gs, int n_chunks,
+                                                            uint16_t* __restrict__ out) {
+    const int lane = threadIdx.x, qg = lane >> 4, n = lane & 15;
+    const int chunk = blockIdx.x % n_chunks, kvh = (blockIdx.x / n_chunks) % n_kv_heads;
+    const int64_t b = blockIdx.x / (n_chunks * n_kv_heads);
+    const int hq = kvh * gs + 4 * chunk + qg;
+    const bool q_ok = 4 * chunk + qg < gs;
+    const float* p = ws + (b * n_q_heads + (q_ok ? hq : kvh * gs)) * (int64_t)n_splits * kPart;
+    // split maxima: lane n of a query row reads splits n, n+16, ... in parallel
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, p[s * kPart]);
-    float L = 0.0f, A = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < n_splits; ++s) {
-            const float ms = p[s * kPart];
-            if (ms == -INFINITY) continue;              // split without tokens
-            const float f = exp2f(ms - M);
-            L = fmaf(p[s * kPart + 1], f, L);
-            A = fmaf(p[s * kPart + 2 + d], f, A);
+    for (int s = n; s < n_splits; s += 16) M = fmaxf(M, p[s * kPart]);
+    M = row_max16(M);
+    float L = 0.0f, a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = 0.0f;
+    if (M != -INFINITY) {                                // uniform per query row
+        for (int c0 = 0; c0 < n_splits; c0 += 16) {
+            // weight of split c0 + n (zero for splits without tokens: their acc is zero)
+            float fm = 0.0f;
+            if (c0 + n < n_splits) {
+                const float ms = p[(c0 + n) * kPart];
+                if (ms != -INFINITY) {
+                    fm = exp2f(ms - M);
+                    L = fmaf(p[(c0 + n) * kPart + 1], fm, L);
+                }
+            }
+            // all 16 slots are read (indices clamped into range); slots past the
+            // last split carry weight zero, so their loads can all be in flight
+            const int last = min(16, n_splits - c0) - 1;
+            const float* pc = p + c0 * kPart + kAcc + 8 * n;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float f = __shfl(fm, 16 * qg + i);
+                const int si = min(i, last);
+                const float4 x0 = *reinterpret_cast<const float4*>(pc + si * kPart);
+                const float4 x1 = *reinterpret_cast<const float4*>(pc + si * kPart + 4);
+                a[0] = fmaf(x0.x, f, a[0]), a[1] = fmaf(x0.y, f, a[1]), a[2] = fmaf(x0.z, f, a[2]), a[3] = fmaf(x0.w, f, a[3]);
+                a[4] = fmaf(x1.x, f, a[4]), a[5] = fmaf(x1.y, f, a[5]), a[6] = fmaf(x1.z, f, a[6]), a[7] = fmaf(x1.w, f, a[7]);
+            }
         }
+        L = row_sum16(L);
     }
-    sO[d] = L > 0.0f ? A / L : 0.0f;
-    __syncthreads();
-    for (int s = 1; s < kN; s <<= 1) {               // inverse rotation, unnormalised
-        float a = sO[d], c = sO[d ^ s];
-        __syncthreads();
-        sO[d] = (d & s) ? (c - a) : (a + c);
-        __syncthreads();
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] *= inv;
+    fwht_regs<8>(a);
+    const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
+    const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppXor1>(a[i]), s1, a[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppXor2>(a[i]), s2, a[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<0x128>(a[i]), s3, a[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppHalfMirror>(a[i]), s4, a[i]);
+    if (q_ok) {
+        const float sg = mask_sign(kWhtSigma, n) * kInvSqrtN;
+        uint32_t h[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            h[k] = f32_to_f16_bits_sat(a[2 * k] * sg) | (f32_to_f16_bits_sat(a[2 * k + 1] * sg) << 16);
+        *reinterpret_cast<uint4*>(out + (b * n_q_heads + hq) * kN + 8 * out_group(n)) = make_uint4(h[0], h[1], h[2], h[3]);
     }
-    out[row * kN + d] = (uint16_t)f32_to_f16_bits_sat(sO[d] * kInvSqrtN);
 }
 
 template <int BK, int BV>
@@ -480,7 +527,8 @@ hipError_t launch_bits(const DecodeArgs& a) {
 }  // namespace
 
 // Split-K plan: tiles of one (sequence, KV head) are cut into n_splits ranges
-// of tiles_per_split tiles, one wave each, aiming at about 8 waves per CU.
+// of tiles_per_split tiles, one wave each, aiming at about 4 waves per CU
+// (one per SIMD): longer splits amortise the pipeline start and the merge.
 void decode_split_plan(int64_t batch, int n_kv_heads, int n_q_heads, int max_tiles, int* n_splits,
                        int* tiles_per_split) {
     if (max_tiles <= 0) {
@@ -490,7 +538,7 @@ void decode_split_plan(int64_t batch, int n_kv_heads, int n_q_heads, int max_til
     }
     const int gs = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 1;
     const int64_t heads = batch * (int64_t)n_kv_heads * ((gs + 3) / 4);
-    int64_t want = heads > 0 ? (2048 + heads - 1) / heads : 1;
+    int64_t want = heads > 0 ? (1024 + heads - 1) / heads : 1;
     if (want < 1) want = 1;
     if (want > max_tiles) want = max_tiles;
     const int tps = (int)((max_tiles + want - 1) / want);
@@ -505,8 +553,9 @@ hipError_t launch_decode(const DecodeArgs& a) {
     else
         e = a.bits_v == 2 ? launch_bits<4, 2>(a) : launch_bits<4, 4>(a);
     if (e != hipSuccess) return e;
-    decode_combine_kernel<<<dim3((unsigned)(a.batch * a.n_q_heads)), dim3(kN), 0, a.stream>>>(a.workspace,
-                                                                                             a.n_splits, a.out);
+    const int gs = a.n_q_heads / a.n_kv_heads, n_chunks = (gs + 3) / 4;
+    decode_combine_kernel<<<dim3((unsigned)(a.batch * a.n_kv_heads * n_chunks)), dim3(64), 0, a.stream>>>(
+        a.workspace, a.n_splits, a.n_q_heads, a.n_kv_heads, gs, n_chunks, a.out);
     return hipGetLastError();
 }
 

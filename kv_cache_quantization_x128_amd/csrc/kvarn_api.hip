@@ -104,7 +104,7 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
     if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0) return 0;
     int n_splits = 1, tps = 1;
     kvarn::decode_split_plan(batch, n_kv_heads, n_q_heads, max_tiles, &n_splits, &tps);
-    return (size_t)batch * (size_t)n_q_heads * (size_t)n_splits * (size_t)(2 + KVARN_HEAD_DIM) * sizeof(float);
+    return (size_t)batch * (size_t)n_q_heads * (size_t)n_splits * (size_t)kvarn::kDecodePart * sizeof(float);
 }
 
 int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,

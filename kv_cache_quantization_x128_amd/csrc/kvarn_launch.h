@@ -30,6 +30,10 @@ struct DequantizeArgs {
     hipStream_t stream;
 };
 
+// Floats per split-K partial of decode attention: m, l, 6 unused, acc[128]
+// (a multiple of 4 so that every acc[] starts 16-byte aligned).
+constexpr int kDecodePart = 136;
+
 struct DecodeArgs {
     const uint16_t* q;
     const uint8_t* k_packed;

@@ -97,6 +97,6 @@ def test_decode_argument_errors():
 
 def test_decode_workspace_plan():
     # 16 sequences x 8 KV heads x 256 tiles -> 16 splits of 16 tiles
-    assert kvarn.workspace_bytes(16, 32, 8, 256) == 16 * 32 * 16 * 130 * 4
-    assert kvarn.workspace_bytes(1, 4, 1, 3) == 1 * 4 * 3 * 130 * 4
-    assert kvarn.workspace_bytes(2, 4, 1, 0) == 2 * 4 * 1 * 130 * 4
+    assert kvarn.workspace_bytes(16, 32, 8, 256) == 16 * 32 * 8 * 136 * 4
+    assert kvarn.workspace_bytes(1, 4, 1, 3) == 1 * 4 * 3 * 136 * 4
+    assert kvarn.workspace_bytes(2, 4, 1, 0) == 2 * 4 * 1 * 136 * 4
