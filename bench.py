@@ -162,6 +162,8 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
             fn = lambda: kvarn.decode_attn(q, kr, vr, n_tiles, hkv, nt, bits, bits, out=out, workspace=ws)  # noqa
             timer(fn) if timed else fn()
 
+    # eager: HIP events around every call (includes the host's launch overhead
+    # whenever the host is slower than the GPU)
     for _ in range(warmup):
         one_pass(False)
     torch.cuda.synchronize()
@@ -170,7 +172,26 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
         one_pass(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    layer_ms = timer.mean_ms()
+    eager_ms = timer.mean_ms()
+    ref = out.clone()
+    # the same pass captured once in a HIP graph and replayed: device time per layer
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass(False)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        raise RuntimeError("decode attention: graph replay differs from the eager pass")
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(passes):
+        graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    layer_ms = s.elapsed_time(e) / (passes * layers)
+    if not torch.equal(out, ref):
+        raise RuntimeError("decode attention: graph replay differs from the eager pass")
     pb = kvarn.tile_bytes(bits)
     alg_bytes = 2 * batch * hkv * nt * pb + 2 * batch * hq * 128 * 2
     ach = alg_bytes / (layer_ms * 1e-3) / 1e9
@@ -178,7 +199,9 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
         "workload": f"decode attention: batch {batch}, {hq} query heads on {hkv} KV heads, head_dim 128, "
                     f"{tokens}-token {bits}-bit K/V cache, {layers} layers",
         "layer_ms": layer_ms,
-        "wall_s_per_pass": wall / passes,
+        "timing": f"HIP events around {passes} replays of a HIP graph holding the {layers}-layer pass",
+        "eager_layer_ms": eager_ms,
+        "eager_wall_s_per_pass": wall / passes,
         "fp16_equiv_GBs": 2 * batch * hkv * nt * TILE_F16_BYTES / (layer_ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode_mfma"),
