@@ -171,7 +171,8 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
  *   n_q_heads       multiple of n_kv_heads, at most 8 query heads per KV head;
  *                   batch and n_kv_heads at most 65535
  *   bits_k, bits_v  2 or 4
- *   sm_scale        softmax scale, 1/sqrt(128) for standard attention
+ *   sm_scale        softmax scale, 1/sqrt(128) for standard attention; zero or
+ *                   2^-32 <= |sm_scale| <= 2^32 (KVARN_EINVAL otherwise)
  *   workspace       device, >= kvarn_decode_attn_workspace_bytes(...) bytes,
  *                   16-byte aligned; contents on entry do not matter
  *

@@ -21,9 +21,11 @@ ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
 # -fno-honor-nans: inputs are finite by contract (include/kvarn.h), so min / max
 # need no NaN canonicalisation and fold their DPP source moves.
+# -amdgpu-mfma-vgpr-form: matrix-core results land in ordinary VGPRs (no
+# accumulator-register reads after every product).
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-fno-honor-nans",
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

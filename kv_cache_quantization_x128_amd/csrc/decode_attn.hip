@@ -100,17 +100,18 @@ __device__ __forceinline__ void fp8_slot(int k, int& gl, int& s) {
 // zero with no memory access: used for tiles past the end or with an invalid
 // block-table entry, so that every iteration issues the same loads).
 constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kAuxStream = 2;   // cache policy of the record loads: non-temporal (read once)
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), (short)0, bytes, kRsrcWord3);
 }
 __device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAuxStream);
     return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxStream);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -165,27 +166,33 @@ __device__ __forceinline__ void f16x8(uint4 b, float (&v)[8]) {
 // Split 8 values (positions 8J..8J+7 of the lane's query) into PIECES E4M3
 // pieces and write them as dwords into the A staging buffer of the wave
 // (64 lanes x 32 bytes; rows m = 4 query + piece).  off_e / off_o: byte offsets
-// of the piece-0 dword of the even / odd positions.
+// of the piece-0 dwords of the even / odd positions.  Piece k is the nearest
+// E4M3 value of 16^k times what the earlier pieces left; the scaled conversions
+// divide by (encode) or multiply by (decode) the power of two 16^-k exactly,
+// so the residual never needs rescaling.
+typedef short v2s __attribute__((ext_vector_type(2)));
 template <int PIECES>
 __device__ __forceinline__ void write_pieces(uint8_t* __restrict__ stage, int off_e, int off_o, const float (&u0)[8]) {
-    float u[8];
+    float r[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = u0[i];
+    for (int i = 0; i < 8; ++i) r[i] = u0[i];
 #pragma unroll
     for (int k = 0; k < PIECES; ++k) {
-        int e = 0, o = 0;
-        e = __builtin_amdgcn_cvt_pk_fp8_f32(u[0], u[2], e, false);
-        e = __builtin_amdgcn_cvt_pk_fp8_f32(u[4], u[6], e, true);
-        o = __builtin_amdgcn_cvt_pk_fp8_f32(u[1], u[3], o, false);
-        o = __builtin_amdgcn_cvt_pk_fp8_f32(u[5], u[7], o, true);
-        *reinterpret_cast<int*>(stage + off_e + 48 * k) = e;
-        *reinterpret_cast<int*>(stage + off_o + 48 * k) = o;
+        const float sc = k == 0 ? 1.0f : (k == 1 ? 0.0625f : (k == 2 ? 0.00390625f : 0.000244140625f));  // 16^-k
+        v2s e = {0, 0}, o = {0, 0};
+        e = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(e, r[0], r[2], sc, false);
+        e = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(e, r[4], r[6], sc, true);
+        o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, r[1], r[3], sc, false);
+        o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, r[5], r[7], sc, true);
+        const int ei = __builtin_bit_cast(int, e), oi = __builtin_bit_cast(int, o);
+        *reinterpret_cast<int*>(stage + off_e + 48 * k) = ei;
+        *reinterpret_cast<int*>(stage + off_o + 48 * k) = oi;
         if (k + 1 < PIECES) {
             f2 b;
-            b = __builtin_amdgcn_cvt_pk_f32_fp8(e, false); u[0] = 16.0f * (u[0] - b.x), u[2] = 16.0f * (u[2] - b.y);
-            b = __builtin_amdgcn_cvt_pk_f32_fp8(e, true); u[4] = 16.0f * (u[4] - b.x), u[6] = 16.0f * (u[6] - b.y);
-            b = __builtin_amdgcn_cvt_pk_f32_fp8(o, false); u[1] = 16.0f * (u[1] - b.x), u[3] = 16.0f * (u[3] - b.y);
-            b = __builtin_amdgcn_cvt_pk_f32_fp8(o, true); u[5] = 16.0f * (u[5] - b.x), u[7] = 16.0f * (u[7] - b.y);
+            b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ei, sc, false); r[0] -= b.x, r[2] -= b.y;
+            b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ei, sc, true); r[4] -= b.x, r[6] -= b.y;
+            b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(oi, sc, false); r[1] -= b.x, r[3] -= b.y;
+            b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(oi, sc, true); r[5] -= b.x, r[7] -= b.y;
         }
     }
 }
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<0x128>(v[i]), s3, v[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppHalfMirror>(v[i]), s4, v[i]);
-        const float sg = mask_sign(kWhtSigma, n) * kInvSqrtN;
+        const float sg = mask_sign(kWhtSigma, n) * (kInvSqrtN * scale_log2);   // softmax scale folded in
         float mx = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] *= sg, mx = fmaxf(mx, fabsf(v[i]));
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
             for (int blk = 0; blk < 8; ++blk) {
                 // rows of the lane: query qg, pieces 0..3
                 const float raw = (d[blk][0] + d[blk][1]) + (d[blk][2] + d[blk][3]);
-                sc[blk] = (raw + cze) * (s2[blk] * scale_log2);
+                sc[blk] = (raw + cze) * s2[blk];             // log2-domain score
             }
         }
         // ---- online softmax over this tile (per query: the 16 lanes of a row)
@@ -455,39 +462,40 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     const int hq = kvh * gs + 4 * chunk + qg;
     const bool q_ok = 4 * chunk + qg < gs;
     const float* p = ws + (b * n_q_heads + (q_ok ? hq : kvh * gs)) * (int64_t)n_splits * kPart;
-    // split maxima: lane n of a query row reads splits n, n+16, ... in parallel
-    float M = -INFINITY;
-    for (int s = n; s < n_splits; s += 16) M = fmaxf(M, p[s * kPart]);
-    M = row_max16(M);
-    float L = 0.0f, a[8];
+    // every load of a group of 16 splits is issued before any is used: lane n of
+    // a query row reads (m, l) of split c0 + n and the lane's acc slices of all
+    // 16 (indices clamped into range; slots past the last split get weight 0)
+    float M = -INFINITY, L = 0.0f, a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = 0.0f;
-    if (M != -INFINITY) {                                // uniform per query row
-        for (int c0 = 0; c0 < n_splits; c0 += 16) {
-            // weight of split c0 + n (zero for splits without tokens: their acc is zero)
-            float fm = 0.0f;
-            if (c0 + n < n_splits) {
-                const float ms = p[(c0 + n) * kPart];
-                if (ms != -INFINITY) {
-                    fm = exp2f(ms - M);
-                    L = fmaf(p[(c0 + n) * kPart + 1], fm, L);
-                }
-            }
-            // all 16 slots are read (indices clamped into range); slots past the
-            // last split carry weight zero, so their loads can all be in flight
-            const int last = min(16, n_splits - c0) - 1;
-            const float* pc = p + c0 * kPart + kAcc + 8 * n;
+    for (int c0 = 0; c0 < n_splits; c0 += 16) {
+        const int last = min(16, n_splits - c0) - 1;
+        const float2 ml = *reinterpret_cast<const float2*>(p + (c0 + min(n, last)) * kPart);
+        const float* pc = p + c0 * kPart + kAcc + 8 * n;
+        float4 x[16][2];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float f = __shfl(fm, 16 * qg + i);
-                const int si = min(i, last);
-                const float4 x0 = *reinterpret_cast<const float4*>(pc + si * kPart);
-                const float4 x1 = *reinterpret_cast<const float4*>(pc + si * kPart + 4);
-                a[0] = fmaf(x0.x, f, a[0]), a[1] = fmaf(x0.y, f, a[1]), a[2] = fmaf(x0.z, f, a[2]), a[3] = fmaf(x0.w, f, a[3]);
-                a[4] = fmaf(x1.x, f, a[4]), a[5] = fmaf(x1.y, f, a[5]), a[6] = fmaf(x1.z, f, a[6]), a[7] = fmaf(x1.w, f, a[7]);
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int si = min(i, last);
+            x[i][0] = *reinterpret_cast<const float4*>(pc + si * kPart);
+            x[i][1] = *reinterpret_cast<const float4*>(pc + si * kPart + 4);
         }
-        L = row_sum16(L);
+        const float ms = n <= last ? ml.x : -INFINITY;
+        const float m_new = fmaxf(M, row_max16(ms));
+        if (m_new == -INFINITY) continue;                // no tokens so far in this query row
+        const float alpha = exp2f(M - m_new);            // 0 on the first group with tokens
+        const float fm = ms == -INFINITY ? 0.0f : exp2f(ms - m_new);
+        L = fmaf(L, alpha, row_sum16(ml.y * fm));
+        M = m_new;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float f = __shfl(fm, 16 * qg + i);
+            a[0] = fmaf(x[i][0].x, f, a[0]), a[1] = fmaf(x[i][0].y, f, a[1]);
+            a[2] = fmaf(x[i][0].z, f, a[2]), a[3] = fmaf(x[i][0].w, f, a[3]);
+            a[4] = fmaf(x[i][1].x, f, a[4]), a[5] = fmaf(x[i][1].y, f, a[5]);
+            a[6] = fmaf(x[i][1].z, f, a[6]), a[7] = fmaf(x[i][1].w, f, a[7]);
+        }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll

@@ -100,6 +100,17 @@ int kvarn_dequantize_tiles(const void* packed, const int64_t* src_tile_index, in
     return hip_status(kvarn::launch_dequantize(a));
 }
 
+// The softmax scale rides on the query's power-of-two block scale, which must
+// stay inside the E8M0 range: zero, or 2^-32 <= |sm_scale| <= 2^32.
+// (Checked on the bits: the library is built assuming no NaN arithmetic.)
+static bool valid_sm_scale(float s) {
+    uint32_t u;
+    memcpy(&u, &s, sizeof(u));
+    u &= 0x7FFFFFFFu;
+    const uint32_t e = u >> 23;                       // biased exponent; 255 = inf / NaN
+    return u == 0 || (e >= 127 - 32 && (e < 127 + 32 || u == (127u + 32u) << 23));
+}
+
 size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_heads, int max_tiles) {
     if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0) return 0;
     int n_splits = 1, tps = 1;
@@ -113,7 +124,7 @@ int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (q == nullptr || k_packed == nullptr || v_packed == nullptr || n_tiles_per_seq == nullptr ||
         out == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0 || n_records < 0 ||
-        n_q_heads % n_kv_heads != 0 || !(sm_scale == sm_scale))
+        n_q_heads % n_kv_heads != 0 || !valid_sm_scale(sm_scale))
         return KVARN_EINVAL;
     if (!valid_bits(bits_k) || !valid_bits(bits_v) || n_q_heads / n_kv_heads > 8) return KVARN_EUNSUPPORTED;
     if (batch > 65535 || n_kv_heads > 65535) return KVARN_EUNSUPPORTED;  // grid y/z limits

@@ -79,8 +79,9 @@ def test_dequantize_argument_errors():
     assert dq(n=0) == kvarn.OK
 
 
-def da(qp=A, k=A, v=A, bt=None, nt=A, nrec=10, b=2, hq=8, hkv=2, mt=4, bk=2, bv=2, out=A2, ws=A, wsb=1 << 20):
-    return kvarn.load().kvarn_decode_attn(qp, k, v, bt, nt, nrec, b, hq, hkv, mt, bk, bv, 0.088, out, ws, wsb, None)
+def da(qp=A, k=A, v=A, bt=None, nt=A, nrec=10, b=2, hq=8, hkv=2, mt=4, bk=2, bv=2, out=A2, ws=A, wsb=1 << 20,
+       sm=0.088):
+    return kvarn.load().kvarn_decode_attn(qp, k, v, bt, nt, nrec, b, hq, hkv, mt, bk, bv, sm, out, ws, wsb, None)
 
 
 def test_decode_argument_errors():
@@ -93,6 +94,10 @@ def test_decode_argument_errors():
     assert da(ws=None) == kvarn.EWORKSPACE
     assert da(wsb=16) == kvarn.EWORKSPACE
     assert da(b=0) == kvarn.OK
+    for sm in (float("nan"), float("inf"), 2.0 ** 33, -(2.0 ** 33), 2.0 ** -33):
+        assert da(sm=sm) == kvarn.EINVAL, sm
+    for sm in (0.0, -0.088, 2.0 ** 32, 2.0 ** -32):
+        assert da(b=0, sm=sm) == kvarn.OK, sm
 
 
 def test_decode_workspace_plan():

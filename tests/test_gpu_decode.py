@@ -52,6 +52,23 @@ def test_decode_small_gqa_bits_ragged(dev, gs, bk, bv):
     assert err.max() <= TOL
 
 
+@pytest.mark.parametrize("sm_scale", [0.0, 2.0 ** -20, 0.5, -0.088, 3.0])
+def test_decode_softmax_scales(dev, sm_scale):
+    """Softmax scales from zero (uniform weights) to sharp, and negative."""
+    batch, hkv, hq, max_tiles = 2, 2, 8, 3
+    kr, vr = _cache(batch * hkv * max_tiles, 2, 2, seed=41)
+    q = np.random.default_rng(42).standard_normal((batch, hq, 128)).astype(np.float16)
+    n_tiles = np.array([3, 2], np.int32)
+    out = kvarn.decode_attn(torch.from_numpy(q).to(dev), torch.from_numpy(kr).to(dev), torch.from_numpy(vr).to(dev),
+                            torch.from_numpy(n_tiles).to(dev), hkv, max_tiles, 2, 2, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    ref = oracle.decode_attn(q.view(np.uint16), kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2, sm_scale=sm_scale)
+    err = parity.rel_l2_rows(got, ref)
+    _log("sm_scale", sm_scale, "max rel l2", err.max())
+    assert err.max() <= TOL
+
+
 def test_decode_block_table_empty_and_out_of_range(dev):
     """Paged records through a block table; an empty sequence gives zeros; table
     entries outside the record buffer contribute nothing."""
@@ -133,3 +150,24 @@ def test_decode_graph_replay_matches_eager(dev):
         torch.cuda.synchronize()
         _log("replay", i, "max abs diff", (out.float() - want.float()).abs().max().item())
         assert torch.equal(out, want)
+
+
+def test_decode_workspace_reuse_across_shapes(dev):
+    """One workspace serves calls of different shapes in turn, whatever the
+    earlier calls left in it: each result equals, bit for bit, the same call on
+    a fresh workspace."""
+    kr, vr = _cache(40, 4, 2, seed=31)
+    kr, vr = torch.from_numpy(kr).to(dev), torch.from_numpy(vr).to(dev)
+    rng = np.random.default_rng(32)
+    shapes = [(3, 8, 2, 6, [6, 4, 1]), (1, 4, 1, 2, [2]), (5, 8, 1, 8, [8, 3, 0, 7, 5]), (3, 8, 2, 6, [2, 6, 5])]
+    big = max(kvarn.workspace_bytes(b, hq, hkv, mt) for b, hq, hkv, mt, _ in shapes)
+    ws = torch.full((big,), 0x7F, dtype=torch.uint8, device=dev)
+    for b, hq, hkv, mt, nts in shapes:
+        q = torch.from_numpy(rng.standard_normal((b, hq, 128)).astype(np.float16)).to(dev)
+        nt = torch.tensor(nts, dtype=torch.int32, device=dev)
+        table = torch.from_numpy(rng.integers(0, 40, size=b * hkv * mt).astype(np.int32)).to(dev)
+        got = kvarn.decode_attn(q, kr, vr, nt, hkv, mt, 4, 2, block_table=table, workspace=ws)
+        want = kvarn.decode_attn(q, kr, vr, nt, hkv, mt, 4, 2, block_table=table)
+        torch.cuda.synchronize()
+        _log("shape", (b, hq, hkv, mt), "max abs diff", (got.float() - want.float()).abs().max().item())
+        assert torch.equal(got, want)
