@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 from kv_cache_quantization_x128_amd import kvarn, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak (counts packed FP32 FMA)
+FP32_VECTOR_PEAK_TFLOPS = 157.3      # published, with packed fp32 FMA
+FP32_NONPACKED_PEAK_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop x 2.4 GHz: the code is built without packed fp32   # MI355X published fp32 vector peak (counts packed FP32 FMA)
 TILE_F16_BYTES = 128 * 128 * 2
 
 
@@ -320,6 +321,8 @@ def main():
         "frac_of_hbm_peak": value / HBM_PEAK_GBS,
         "roofline": {"bound": "alu", "kernel": "quantize_kernel", "achieved": q_tflops,
                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": q_tflops / FP32_VECTOR_PEAK_TFLOPS,
+                     "peak_non_packed_fp32": FP32_NONPACKED_PEAK_TFLOPS,
+                     "frac_non_packed_fp32": q_tflops / FP32_NONPACKED_PEAK_TFLOPS,
                      "traffic": measured_traffic("quantize"), "algorithmic_flops_per_launch": q_flops,
                      "algorithmic_bytes_per_launch": q_alg, "hbm_GBs": q_ach, "hbm_frac": q_ach / HBM_PEAK_GBS},
         "ops": ops,
