@@ -33,7 +33,7 @@ from kv_cache_quantization_x128_amd import kvarn, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3      # published, with packed fp32 FMA
-FP32_NONPACKED_PEAK_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop x 2.4 GHz: the code is built without packed fp32   # MI355X published fp32 vector peak (counts packed FP32 FMA)
+FP32_NONPACKED_PEAK_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop x 2.4 GHz: the code is built without packed fp32
 TILE_F16_BYTES = 128 * 128 * 2
 
 
