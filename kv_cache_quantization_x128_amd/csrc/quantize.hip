@@ -48,6 +48,8 @@
 //                     8 codes of one code row (K: a token's 8 channels, V: a
 //                     channel's 8 tokens) into 16 (2-bit) or 32 (4-bit) bits
 //                     and stores them straight into the record.
+#include <type_traits>
+
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
 
@@ -69,7 +71,6 @@ constexpr float kMagic = 8388608.0f;                 // 2^23: x + 2^23 rounds x 
 // lane through the butterflies (x_lo + x_hi in the lower lane, x_hi - x_lo in
 // the upper one).
 constexpr uint32_t kWhtS1 = 0x5a5a, kWhtS2 = 0x3c3c, kWhtS3 = 0xff00, kWhtS4 = 0x9696, kWhtSigma = 0x09f6;
-constexpr int kDppRor8 = 0x128;
 __device__ __forceinline__ int out_group(int cg) { return (cg & 4) ? (cg ^ 3) : cg; }
 __device__ __forceinline__ float mask_sign(uint32_t mask, int cg) { return ((mask >> cg) & 1u) ? -1.0f : 1.0f; }
 
@@ -134,24 +135,64 @@ __device__ __forceinline__ void col_rs(const float (&v)[16], float (&z)[4]) {
 // of a DPP row.  Lane cg returns kinds 0 and 1 of row 4*b3 + 2*b2 + b1 (b_i = bit
 // i of cg) in z[0], z[1]; lanes cg and cg^1 hold the same result.  Each split
 // stage keeps one half of the values per lane and adds the partner's copy of
-// that half (the partner keeps the other half).
+// that half (the partner keeps the other half).  The split on bit 3 pairs bank
+// 0,1 lanes with bank 2,3 lanes and the split on bit 2 banks 0,2 with 1,3, so
+// those stages write each half with its own bank mask instead of selecting;
+// the split on bit 1 is inside a bank and selects.
+#define KVARN_RS_PAIR(OPC, CTRL, MLO, MHI, u, lo, hi)                                           \
+    OPC " %" #u ", %" #lo ", %" #lo " " CTRL " row_mask:0xf bank_mask:" MLO "\n\t"               \
+    OPC " %" #u ", %" #hi ", %" #hi " " CTRL " row_mask:0xf bank_mask:" MHI "\n\t"
 template <class OP0, class OP1>
 __device__ __forceinline__ void row_rs(const float (&v)[16], int cg, float (&z)[2]) {
-    const bool b3 = cg & 8, b2 = cg & 4, b1 = cg & 2;
-    float u[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const float keep = b3 ? v[m + 8] : v[m], give = b3 ? v[m] : v[m + 8];
-        const float p = dpp<kDppRor8>(give);
-        u[m] = (m & 1) ? OP1::f(keep, p) : OP0::f(keep, p);
+    constexpr bool kSum = std::is_same<OP0, OpSum>::value && std::is_same<OP1, OpSum>::value;
+    static_assert(kSum || (std::is_same<OP0, OpMin>::value && std::is_same<OP1, OpMax>::value), "row_rs ops");
+    float u[8], w4[4];
+    if constexpr (kSum) {
+        asm("s_nop 1\n\t"
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_ror:8", "0x3", "0xc", 0, 8, 16)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_ror:8", "0x3", "0xc", 1, 9, 17)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_ror:8", "0x3", "0xc", 2, 10, 18)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_ror:8", "0x3", "0xc", 3, 11, 19)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_ror:8", "0x3", "0xc", 4, 12, 20)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_ror:8", "0x3", "0xc", 5, 13, 21)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_ror:8", "0x3", "0xc", 6, 14, 22)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_ror:8", "0x3", "0xc", 7, 15, 23)
+            "s_nop 1"
+            : "=&v"(u[0]), "=&v"(u[1]), "=&v"(u[2]), "=&v"(u[3]), "=&v"(u[4]), "=&v"(u[5]), "=&v"(u[6]), "=&v"(u[7])
+            : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+              "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+        asm("s_nop 1\n\t"
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_half_mirror", "0x5", "0xa", 0, 4, 8)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_half_mirror", "0x5", "0xa", 1, 5, 9)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_half_mirror", "0x5", "0xa", 2, 6, 10)
+            KVARN_RS_PAIR("v_add_f32_dpp", "row_half_mirror", "0x5", "0xa", 3, 7, 11)
+            "s_nop 1"
+            : "=&v"(w4[0]), "=&v"(w4[1]), "=&v"(w4[2]), "=&v"(w4[3])
+            : "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(u[4]), "v"(u[5]), "v"(u[6]), "v"(u[7]));
+    } else {
+        asm("s_nop 1\n\t"
+            KVARN_RS_PAIR("v_min_f32_dpp", "row_ror:8", "0x3", "0xc", 0, 8, 16)
+            KVARN_RS_PAIR("v_max_f32_dpp", "row_ror:8", "0x3", "0xc", 1, 9, 17)
+            KVARN_RS_PAIR("v_min_f32_dpp", "row_ror:8", "0x3", "0xc", 2, 10, 18)
+            KVARN_RS_PAIR("v_max_f32_dpp", "row_ror:8", "0x3", "0xc", 3, 11, 19)
+            KVARN_RS_PAIR("v_min_f32_dpp", "row_ror:8", "0x3", "0xc", 4, 12, 20)
+            KVARN_RS_PAIR("v_max_f32_dpp", "row_ror:8", "0x3", "0xc", 5, 13, 21)
+            KVARN_RS_PAIR("v_min_f32_dpp", "row_ror:8", "0x3", "0xc", 6, 14, 22)
+            KVARN_RS_PAIR("v_max_f32_dpp", "row_ror:8", "0x3", "0xc", 7, 15, 23)
+            "s_nop 1"
+            : "=&v"(u[0]), "=&v"(u[1]), "=&v"(u[2]), "=&v"(u[3]), "=&v"(u[4]), "=&v"(u[5]), "=&v"(u[6]), "=&v"(u[7])
+            : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+              "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+        asm("s_nop 1\n\t"
+            KVARN_RS_PAIR("v_min_f32_dpp", "row_half_mirror", "0x5", "0xa", 0, 4, 8)
+            KVARN_RS_PAIR("v_max_f32_dpp", "row_half_mirror", "0x5", "0xa", 1, 5, 9)
+            KVARN_RS_PAIR("v_min_f32_dpp", "row_half_mirror", "0x5", "0xa", 2, 6, 10)
+            KVARN_RS_PAIR("v_max_f32_dpp", "row_half_mirror", "0x5", "0xa", 3, 7, 11)
+            "s_nop 1"
+            : "=&v"(w4[0]), "=&v"(w4[1]), "=&v"(w4[2]), "=&v"(w4[3])
+            : "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(u[4]), "v"(u[5]), "v"(u[6]), "v"(u[7]));
     }
-    float w4[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const float keep = b2 ? u[m + 4] : u[m], give = b2 ? u[m] : u[m + 4];
-        const float p = dpp<kDppHalfMirror>(give);
-        w4[m] = (m & 1) ? OP1::f(keep, p) : OP0::f(keep, p);
-    }
+    const bool b1 = cg & 2;
     float x2[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -162,6 +203,7 @@ __device__ __forceinline__ void row_rs(const float (&v)[16], int cg, float (&z)[
     z[0] = OP0::f(x2[0], dpp<kDppXor1>(x2[0]));
     z[1] = OP1::f(x2[1], dpp<kDppXor1>(x2[1]));
 }
+#undef KVARN_RS_PAIR
 
 // Sum over all 64 lanes of a wave (every lane gets the same value).
 __device__ __forceinline__ float wave_sum(float v) {
@@ -435,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
     constexpr float kL = (float)R::kL;
     const int64_t rec_idx = dst_index ? dst_index[tile] : tile;
     uint8_t* rec = packed + rec_idx * (int64_t)R::kBytes;
-    float inv_s1[8], zoff[8];   // per column (K) or per row (V) of this lane's block
+    float inv_s1[8], zoff[8];   // 1/(L s1) and -z/(L s1) per column (K) or per row (V) of this lane's block
     if constexpr (AXIS == kAxisK) {
         // gauge: mean of r over the 128 tokens (each row owned by a lane pair)
         float part = wave_sum((cg & 1) ? 0.0f : gr);
@@ -479,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
                 rec[R::kS1 + ch] = (uint8_t)c1;
                 *reinterpret_cast<uint16_t*>(rec + R::kZ + 2 * ch) = (uint16_t)zb;
             }
-            const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1));
+            const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1)) * (1.0f / kL);   // 1 / (L s1)
             pub[2 * k] = is1, pub[2 * k + 1] = -f16_bits_to_f32(zb) * is1;
         }
         col_bcast(sm, w, cg, hl, make_float4(pub[0], pub[1], pub[2], pub[3]), inv_s1, zoff);
@@ -523,13 +565,14 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
             rec[R::kS1 + tok] = (uint8_t)c1;
             *reinterpret_cast<uint16_t*>(rec + R::kZ + 2 * tok) = (uint16_t)zb;
         }
-        const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1));
+        const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1)) * (1.0f / kL);     // 1 / (L s1)
         row_bcast(sm, w, rg, a_own, is1, -f16_bits_to_f32(zb) * is1, inv_s1, zoff);
     }
 
     // ---- 4. codes -------------------------------------------------------------------
-    // t = (Zn - z) / s1 clamped to [0, L]; adding 2^23 rounds it to the nearest
-    // integer (ties to even) in the low mantissa bits.  Code rows follow the s2
+    // t = (Zn - z) / (L s1) clamped to [0, 1] (the clamp bit of the FMA), then
+    // L t + 2^23 in one more FMA rounds L t to the nearest integer (ties to
+    // even) in the low mantissa bits: clamp(rint((Zn - z) / s1), 0, L).  Code rows follow the s2
     // axis: K packs the 8 channels of each of the lane's tokens (token rows), V
     // the 8 tokens of each of its channels (channel rows).  The shifted sums of
     // the 2^23 bit patterns are a constant, removed once per packed word.
@@ -546,8 +589,8 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int gi = (AXIS == kAxisK) ? j : a;
-            float t = fmaf(y[a][j], inv_s1[gi], zoff[gi]);
-            t = __builtin_amdgcn_fmed3f(t, 0.0f, kL) + kMagic;
+            float t = __builtin_amdgcn_fmed3f(fmaf(y[a][j], inv_s1[gi], zoff[gi]), 0.0f, 1.0f);
+            t = fmaf(t, kL, kMagic);
             if constexpr (AXIS == kAxisK)
                 word[a] += __float_as_uint(t) << (BITS * j);
             else
