@@ -119,7 +119,11 @@ __device__ __forceinline__ void store_row8(void* __restrict__ out, int64_t e0, b
         }
         uint16_t* p = reinterpret_cast<uint16_t*>(out) + e0;
         if (vec) {
-            *reinterpret_cast<uint4*>(p) = make_uint4(q[0], q[1], q[2], q[3]);
+            // non-temporal: the tile is written once and not read back here; plain
+            // stores leave dirty lines whose write-back slows the next kernel
+            typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+            const u4v qq = {q[0], q[1], q[2], q[3]};
+            __builtin_nontemporal_store(qq, reinterpret_cast<u4v*>(p));
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) p[2 * k] = (uint16_t)q[k], p[2 * k + 1] = (uint16_t)(q[k] >> 16);

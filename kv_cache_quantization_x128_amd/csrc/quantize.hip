@@ -231,12 +231,17 @@ struct Smem {
     float gsum[4];          // per wave: gauge partial sums
 };
 
+// The tile is read once: non-temporal loads keep the stream of tiles from
+// evicting what the caches hold (the records this kernel writes among them).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int DT>
 __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, bool vec, float (&v)[8]) {
     if constexpr (DT == kF32) {
         const float* p = reinterpret_cast<const float*>(x) + e0;
         if (vec) {
-            const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+            const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+            const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
             v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
         } else {
 #pragma unroll
@@ -246,7 +251,7 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, bo
         const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + e0;
         uint32_t w[4];
         if (vec) {
-            const uint4 q = *reinterpret_cast<const uint4*>(p);
+            const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
             w[0] = q.x, w[1] = q.y, w[2] = q.z, w[3] = q.w;
         } else {
 #pragma unroll
