@@ -235,6 +235,8 @@ struct Smem {
 // evicting what the caches hold (the records this kernel writes among them).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
 template <int DT>
 __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, bool vec, float (&v)[8]) {
     if constexpr (DT == kF32) {
@@ -267,6 +269,18 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, bo
                 v[2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
             }
         }
+    }
+}
+
+// Raw dwords of 8 consecutive 16-bit elements (non-temporal like load8).
+__device__ __forceinline__ void load8_raw(const void* __restrict__ x, int64_t e0, bool vec, uint32_t* w) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + e0;
+    if (vec) {
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        w[0] = q.x, w[1] = q.y, w[2] = q.z, w[3] = q.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = (uint32_t)p[2 * k] | ((uint32_t)p[2 * k + 1] << 16);
     }
 }
 
@@ -321,8 +335,11 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int rg = lane >> 4, cg = lane & 15, hl = lane >> 4;  // hl = (bit 5, bit 4) = rg
-    const int og = out_group(cg);                                // output channel group of this lane
-    const float sig = mask_sign(kWhtSigma, cg);                  // sign of this lane's rotated values
+    // output channel group of this lane and the sign of its rotated values: the
+    // 16-bit path rotates on the matrix cores in natural order, the fp32 path
+    // with the DPP network (permuted groups, known signs)
+    const int og = DT == kF32 ? out_group(cg) : cg;
+    const float sig = DT == kF32 ? mask_sign(kWhtSigma, cg) : 1.0f;
     const int row0 = 32 * w + 8 * rg;                            // first token of this lane's block
     const int a_own = 4 * ((cg >> 3) & 1) + 2 * ((cg >> 2) & 1) + ((cg >> 1) & 1);  // row owned after row_rs
     const int jc0 = 2 * hl;                                      // first local column owned after col_rs
@@ -331,8 +348,8 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
 
     // ---- 1. load and rotate ------------------------------------------------------
     float y[8][8];
-    {
-        const bool vec = ((start | token_stride) & 7) == 0;
+    const bool vec = ((start | token_stride) & 7) == 0;
+    if constexpr (DT == kF32) {
 #pragma unroll
         for (int a = 0; a < 8; ++a) load8<DT>(x, start + (int64_t)(row0 + a) * token_stride + 8 * cg, vec, y[a]);
         const float s1 = mask_sign(kWhtS1, cg), s2 = mask_sign(kWhtS2, cg);
@@ -349,6 +366,50 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
         for (int a = 0; a < 8; ++a) KVARN_FMAC_DPP8(y[a], s3, "row_ror:8");
 #pragma unroll
         for (int a = 0; a < 8; ++a) KVARN_FMAC_DPP8(y[a], s4, "row_half_mirror");
+    } else {
+        // Channel c = 8g + j (g = group, j = 0..7): H128 = H16 (over g) x H8
+        // (over j).  The H16 half is a 16 x 16 x 16 matrix-core product per j
+        // on the raw 16-bit inputs (exact products, fp32 sums): rows are 16
+        // tokens, K the 16 input groups, B the +-1 matrix H16, so lane
+        // (rg, cg) receives tokens 4rg + i of the product for output group cg.
+        // Product s = 0, 1 takes tokens 8(m/4) + 4s + m%4 as its rows m, which
+        // hands the lane tokens 8rg + 4s + i: its usual 8 x 8 block.  The H8
+        // half then runs in-lane over j.
+        const int m = lane & 15, q = lane >> 4;
+        s16x4 hb;   // B: H16[k = 4q + i][n = m] as bf16 / f16 +-1
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool neg = __builtin_popcount((4 * q + i) & m) & 1;
+            const uint16_t one = DT == kBF16 ? 0x3F80u : 0x3C00u;
+            hb[i] = (short)(neg ? (one | 0x8000u) : one);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int tok = 32 * w + 8 * (m >> 2) + 4 * s + (m & 3);
+            uint32_t dw[16];   // channels 32q .. 32q + 31 of the token, two per dword
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                load8_raw(x, start + (int64_t)tok * token_stride + 32 * q + 8 * c, vec, dw + 4 * c);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // A row m, K slots i = 0..3: channel 32q + 8i + j, in dword 4i + j/2
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t a0 = __builtin_amdgcn_perm(dw[4 + (j >> 1)], dw[j >> 1], sel);
+                const uint32_t a1 = __builtin_amdgcn_perm(dw[12 + (j >> 1)], dw[8 + (j >> 1)], sel);
+                const s16x4 av = __builtin_bit_cast(s16x4, make_uint2(a0, a1));
+                const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                f32x4 d;
+                if constexpr (DT == kBF16)
+                    d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, hb, zero, 0, 0, 0);
+                else
+                    d = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4, av),
+                                                              __builtin_bit_cast(h16x4, hb), zero, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[4 * s + i][j] = d[i];
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < 8; ++a) fwht_regs<8>(y[a]);
     }
     // y = sig * sqrt(128) * Y for this lane's block (Y the normalised rotation)
     float y2[8][8];
