@@ -205,14 +205,21 @@ __device__ __forceinline__ void row_rs(const float (&v)[16], int cg, float (&z)[
 }
 #undef KVARN_RS_PAIR
 
-// Sum over all 64 lanes of a wave (every lane gets the same value).
+// Sum over all 64 lanes of a wave, returned as a wave-uniform value: row sums
+// by DPP, then row 1 += row 0 and row 3 += row 2 (row_bcast:15), row 3 += rows
+// 0-1 (row_bcast:31), and lane 63 read out.
 __device__ __forceinline__ float wave_sum(float v) {
     v += dpp<kDppXor1>(v);
     v += dpp<kDppXor2>(v);
     v += dpp<kDppHalfMirror>(v);
     v += dpp<kDppMirror>(v);
-    v = rs16<OpSum>(v, v);
-    return rs32<OpSum>(v, v);
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
@@ -376,23 +383,24 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict
         // hands the lane tokens 8rg + 4s + i: its usual 8 x 8 block.  The H8
         // half then runs in-lane over j.
         const int m = lane & 15, q = lane >> 4;
-        s16x4 hb;   // B: H16[k = 4q + i][n = m] as bf16 / f16 +-1
+        s16x4 hb;   // B: H16[g' = 4i + q][n = m] in K slot 4q + i, as bf16 / f16 +-1
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool neg = __builtin_popcount((4 * q + i) & m) & 1;
+            const bool neg = __builtin_popcount((4 * i + q) & m) & 1;
             const uint16_t one = DT == kBF16 ? 0x3F80u : 0x3C00u;
             hb[i] = (short)(neg ? (one | 0x8000u) : one);
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int tok = 32 * w + 8 * (m >> 2) + 4 * s + (m & 3);
-            uint32_t dw[16];   // channels 32q .. 32q + 31 of the token, two per dword
+            uint32_t dw[16];   // dw[4c..4c+3]: channels of group 4c + q of the token, two per dword
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                load8_raw(x, start + (int64_t)tok * token_stride + 32 * q + 8 * c, vec, dw + 4 * c);
+                load8_raw(x, start + (int64_t)tok * token_stride + 32 * c + 8 * q, vec, dw + 4 * c);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                // A row m, K slots i = 0..3: channel 32q + 8i + j, in dword 4i + j/2
+                // A row m, K slot 4q + i holds group g' = 4i + q (channel 8g' + j, in dword 4i + j/2);
+                // each load instruction then reads 64 contiguous bytes per token
                 const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
                 const uint32_t a0 = __builtin_amdgcn_perm(dw[4 + (j >> 1)], dw[j >> 1], sel);
                 const uint32_t a1 = __builtin_amdgcn_perm(dw[12 + (j >> 1)], dw[8 + (j >> 1)], sel);
