@@ -332,8 +332,12 @@ __device__ __forceinline__ void row_bcast(Smem& sm, int w, int rg, int a_own, fl
     __builtin_amdgcn_wave_barrier();
 }
 
+// Three workgroups per CU (at most 168 VGPRs): the tile and its squares take
+// 128 registers per lane, and the third workgroup hides the reduction and
+// barrier latencies of the other two.  The few long-lived addresses that no
+// longer fit are spilled once before the normalisation and reloaded after it.
 template <int BITS, int AXIS, int DT>
-__global__ __launch_bounds__(256, 2) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
+__global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
                                                           int64_t token_stride, const int64_t* __restrict__ tile_off,
                                                           int n_iter, uint8_t* __restrict__ packed,
                                                           const int64_t* __restrict__ dst_index) {
