@@ -88,6 +88,23 @@ enum { KVARN_F16 = 0, KVARN_BF16 = 1, KVARN_F32 = 2 };
 /* Which cache a tile belongs to (decides the grouping, see above). */
 enum { KVARN_AXIS_K = 0, KVARN_AXIS_V = 1 };
 
+/*
+ * Method variants (flags of the quantise, dequantise and decode calls).
+ *   0                  KVarN: rotation, n_iter normalisation rounds, RTN.
+ *   KVARN_NO_ROTATION  skip the Walsh-Hadamard rotation (records are in the
+ *                      channel domain).  With n_iter = 0 this is the per-group
+ *                      min-max RTN of KIVI (keys per channel, values per token;
+ *                      paperlayer.ai summary, section 2 Preliminaries, and the
+ *                      KIVI baseline of its appendix I); s2 is then the constant
+ *                      1/2 of the power-of-two gauge, exact, so codes, s1 and z
+ *                      are those of textbook min-max RTN scaled by 2.
+ * Rotation with n_iter = 0 is the Hadamard-only (QuaRot-style) variant the
+ * pages compare against (agihunt.info note, results table).  A record does not
+ * carry its variant: dequantise and decode it with the flags it was written
+ * with.  Unknown flag bits are KVARN_EINVAL.
+ */
+enum { KVARN_NO_ROTATION = 1 };
+
 /* Version of the packed record layout described above. */
 int kvarn_format_version(void);
 
@@ -121,6 +138,7 @@ const char *kvarn_status_string(int status);
  *                   packed + dst_tile_index[i] * kvarn_tile_bytes(bits)
  *   dst_tile_index  device int64[n_tiles], or NULL for the identity; indices
  *                   must be distinct and inside the caller's record buffer
+ *   flags           0 (the method) or KVARN_NO_ROTATION (see above)
  *
  * Alignment: x and packed 16-byte aligned; tile_stride, token_stride and every
  * tile_offset a multiple of 8 elements (16 bytes).  Offsets that are not are
@@ -128,7 +146,7 @@ const char *kvarn_status_string(int status);
  */
 int kvarn_quantize_tiles(const void *x, int x_dtype, int64_t n_tiles, int64_t tile_stride, int64_t token_stride,
                          const int64_t *tile_offset, int bits, int axis, int n_iter, void *packed,
-                         const int64_t *dst_tile_index, hipStream_t stream);
+                         const int64_t *dst_tile_index, int flags, hipStream_t stream);
 
 /*
  * Reconstruct n_tiles tiles from packed records (fused dual-scale dequant and
@@ -141,12 +159,13 @@ int kvarn_quantize_tiles(const void *x, int x_dtype, int64_t n_tiles, int64_t ti
  *                   at element start(i) + t * token_stride + c with
  *                   start(i) = dst_tile_offset ? dst_tile_offset[i] : i * tile_stride
  *   out_dtype       KVARN_F16, KVARN_BF16 (round to nearest even) or KVARN_F32
+ *   flags           the flags the records were written with
  *
  * Alignment as for kvarn_quantize_tiles (out in place of x).
  */
 int kvarn_dequantize_tiles(const void *packed, const int64_t *src_tile_index, int64_t n_tiles, int bits, int axis,
                            void *out, int out_dtype, int64_t tile_stride, int64_t token_stride,
-                           const int64_t *dst_tile_offset, hipStream_t stream);
+                           const int64_t *dst_tile_offset, int flags, hipStream_t stream);
 
 /* Workspace bytes kvarn_decode_attn needs for this shape (split-K partials). */
 size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_heads, int max_tiles);
@@ -175,13 +194,14 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
  *                   2^-32 <= |sm_scale| <= 2^32 (KVARN_EINVAL otherwise)
  *   workspace       device, >= kvarn_decode_attn_workspace_bytes(...) bytes,
  *                   16-byte aligned; contents on entry do not matter
+ *   flags           the flags the K and V records were written with
  *
  * A sequence with no tiles gets a zero output.
  */
 int kvarn_decode_attn(const void *q, const void *k_packed, const void *v_packed, const int32_t *block_table,
                       const int32_t *n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
                       int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, void *out,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+                      void *workspace, size_t workspace_bytes, int flags, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ n_tiles_per_seq, int64_t n_records,
     int n_q_heads, int n_kv_heads, int max_tiles, int tiles_per_split, int n_splits, int gs, int n_chunks,
-    float scale_log2, float* __restrict__ ws) {
+    float scale_log2, float* __restrict__ ws, int rotate) {
     using RK = Rec<BK>;
     using RV = Rec<BV>;
     __shared__ WaveSmem smem[4];
@@ -247,7 +247,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     WaveSmem& sm = smem[w];
 
     // ---- rotated, scaled queries: lane holds channels 8*G..8*G+7 of query qg --
-    const int G = out_group(n);
+    // (without the rotation, KVARN_NO_ROTATION, the lane keeps channels 8n..)
+    const int G = rotate ? out_group(n) : n;
     float qh[8];
     float qexp;                                        // q~ = qh * 2^qexp
     {
@@ -259,18 +260,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = 0.0f;
         }
-        fwht_regs<8>(v);
-        const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
-        const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
+        if (rotate) {
+            fwht_regs<8>(v);
+            const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
+            const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppXor1>(v[i]), s1, v[i]);
+            for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppXor1>(v[i]), s1, v[i]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppXor2>(v[i]), s2, v[i]);
+            for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppXor2>(v[i]), s2, v[i]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<0x128>(v[i]), s3, v[i]);
+            for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<0x128>(v[i]), s3, v[i]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppHalfMirror>(v[i]), s4, v[i]);
-        const float sg = mask_sign(kWhtSigma, n) * (kInvSqrtN * scale_log2);   // softmax scale folded in
+            for (int i = 0; i < 8; ++i) v[i] = fmaf(dpp<kDppHalfMirror>(v[i]), s4, v[i]);
+        }
+        // softmax scale folded in
+        const float sg = rotate ? mask_sign(kWhtSigma, n) * (kInvSqrtN * scale_log2) : scale_log2;
         float mx = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] *= sg, mx = fmaxf(mx, fabsf(v[i]));
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
 // query rotation), FP16.  Lane = (query qg, channels 8n..8n+7).
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws, int n_splits,
                                                             int n_q_heads, int n_kv_heads, int gs, int n_chunks,
-                                                            uint16_t* __restrict__ out) {
+                                                            uint16_t* __restrict__ out, int rotate) {
     const int lane = threadIdx.x, qg = lane >> 4, n = lane & 15;
     const int chunk = blockIdx.x % n_chunks, kvh = (blockIdx.x / n_chunks) % n_kv_heads;
     const int64_t b = blockIdx.x / (n_chunks * n_kv_heads);
@@ -500,24 +504,27 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] *= inv;
-    fwht_regs<8>(a);
-    const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
-    const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
+    if (rotate) {
+        fwht_regs<8>(a);
+        const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
+        const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppXor1>(a[i]), s1, a[i]);
+        for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppXor1>(a[i]), s1, a[i]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppXor2>(a[i]), s2, a[i]);
+        for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppXor2>(a[i]), s2, a[i]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<0x128>(a[i]), s3, a[i]);
+        for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<0x128>(a[i]), s3, a[i]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppHalfMirror>(a[i]), s4, a[i]);
+        for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppHalfMirror>(a[i]), s4, a[i]);
+    }
     if (q_ok) {
-        const float sg = mask_sign(kWhtSigma, n) * kInvSqrtN;
+        const float sg = rotate ? mask_sign(kWhtSigma, n) * kInvSqrtN : 1.0f;
         uint32_t h[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             h[k] = f32_to_f16_bits_sat(a[2 * k] * sg) | (f32_to_f16_bits_sat(a[2 * k + 1] * sg) << 16);
-        *reinterpret_cast<uint4*>(out + (b * n_q_heads + hq) * kN + 8 * out_group(n)) = make_uint4(h[0], h[1], h[2], h[3]);
+        const int og = rotate ? out_group(n) : n;
+        *reinterpret_cast<uint4*>(out + (b * n_q_heads + hq) * kN + 8 * og) = make_uint4(h[0], h[1], h[2], h[3]);
     }
 }
 
@@ -528,7 +535,7 @@ hipError_t launch_bits(const DecodeArgs& a) {
     const dim3 grid((unsigned)((a.n_splits + 3) / 4), (unsigned)(a.n_kv_heads * n_chunks), (unsigned)a.batch);
     decode_mfma_kernel<BK, BV><<<grid, dim3(256), 0, a.stream>>>(
         a.q, a.k_packed, a.v_packed, a.block_table, a.n_tiles_per_seq, a.n_records, a.n_q_heads, a.n_kv_heads,
-        a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace);
+        a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace, a.rotate);
     return hipGetLastError();
 }
 
@@ -563,7 +570,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
     if (e != hipSuccess) return e;
     const int gs = a.n_q_heads / a.n_kv_heads, n_chunks = (gs + 3) / 4;
     decode_combine_kernel<<<dim3((unsigned)(a.batch * a.n_kv_heads * n_chunks)), dim3(64), 0, a.stream>>>(
-        a.workspace, a.n_splits, a.n_q_heads, a.n_kv_heads, gs, n_chunks, a.out);
+        a.workspace, a.n_splits, a.n_q_heads, a.n_kv_heads, gs, n_chunks, a.out, a.rotate);
     return hipGetLastError();
 }
 

@@ -135,7 +135,8 @@ template <int BITS, int AXIS, int ODT>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ packed,
                                                          const int64_t* __restrict__ src_index,
                                                          void* __restrict__ out, int64_t tile_stride,
-                                                         int64_t token_stride, const int64_t* __restrict__ dst_off) {
+                                                         int64_t token_stride, const int64_t* __restrict__ dst_off,
+                                                         int rotate) {
     using R = Rec<BITS>;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int rg = lane >> 4, cg = lane & 15;
@@ -174,7 +175,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
     }
     // Yh times the lane's input sign (and, for V, 1/sqrt(128)); the K row scale
     // s2_t / sqrt(128) is applied after the rotation, which is linear along the row.
-    const float sg = mask_sign(kInSign, cg);
+    // Without the rotation (KVARN_NO_ROTATION) Xh = Yh: no sign, no 1/sqrt(128).
+    const float sg = rotate ? mask_sign(kInSign, cg) : 1.0f;
+    const float nrm = rotate ? kInvSqrtN : 1.0f;
     if constexpr (AXIS == kAxisK) {
         float a1[8], a0[8];
 #pragma unroll
@@ -186,14 +189,14 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
     } else {
         float m2[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m2[j] = sg * kInvSqrtN * s2v[j];
+        for (int j = 0; j < 8; ++j) m2[j] = sg * nrm * s2v[j];
 #pragma unroll
         for (int a = 0; a < 8; ++a)
 #pragma unroll
             for (int j = 0; j < 8; ++j) c[a][j] = fmaf(c[a][j], s1v[a], zv[a]) * m2[j];
     }
     // inverse rotation over the 128 channels of every token
-    {
+    if (rotate) {
         const float s1 = mask_sign(kS1, cg), s2 = mask_sign(kS2, cg);
         const float s3 = mask_sign(kS3, cg), s4 = mask_sign(kS4, cg);
 #pragma unroll
@@ -210,14 +213,14 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
     if constexpr (AXIS == kAxisK) {
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
-            const float f = s2v[a] * kInvSqrtN;
+            const float f = s2v[a] * nrm;
 #pragma unroll
             for (int j = 0; j < 8; ++j) c[a][j] *= f;
         }
     }
     const int64_t start = dst_off ? dst_off[tile] : tile * tile_stride;
     const bool vec = ((start | token_stride) & 7) == 0;
-    const int og = out_group(cg);
+    const int og = rotate ? out_group(cg) : cg;
 #pragma unroll
     for (int a = 0; a < 8; ++a) store_row8<ODT>(out, start + (int64_t)(row0 + a) * token_stride + 8 * og, vec, c[a]);
 }
@@ -228,15 +231,15 @@ hipError_t launch_bits_axis(const DequantizeArgs& a) {
     switch (a.out_dtype) {
     case kF16:
         dequantize_kernel<BITS, AXIS, kF16><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
-                                                                        a.token_stride, a.dst_offset);
+                                                                        a.token_stride, a.dst_offset, a.rotate);
         break;
     case kBF16:
         dequantize_kernel<BITS, AXIS, kBF16><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
-                                                                         a.token_stride, a.dst_offset);
+                                                                         a.token_stride, a.dst_offset, a.rotate);
         break;
     default:
         dequantize_kernel<BITS, AXIS, kF32><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
-                                                                        a.token_stride, a.dst_offset);
+                                                                        a.token_stride, a.dst_offset, a.rotate);
         break;
     }
     return hipGetLastError();

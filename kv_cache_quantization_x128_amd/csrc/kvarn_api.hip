@@ -20,6 +20,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool valid_bits(int b) { return b == 2 || b == 4; }
 bool valid_dtype(int d) { return d == KVARN_F16 || d == KVARN_BF16 || d == KVARN_F32; }
 bool valid_axis(int a) { return a == KVARN_AXIS_K || a == KVARN_AXIS_V; }
+bool valid_flags(int f) { return (f & ~KVARN_NO_ROTATION) == 0; }
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return KVARN_OK;
@@ -71,8 +72,9 @@ int kvarn_parse_preset(const char* preset, int* bits_k, int* bits_v, int* group)
 
 int kvarn_quantize_tiles(const void* x, int x_dtype, int64_t n_tiles, int64_t tile_stride, int64_t token_stride,
                          const int64_t* tile_offset, int bits, int axis, int n_iter, void* packed,
-                         const int64_t* dst_tile_index, hipStream_t stream) {
-    if (!valid_dtype(x_dtype) || !valid_axis(axis) || packed == nullptr || n_iter < 0 || n_iter > 64)
+                         const int64_t* dst_tile_index, int flags, hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || !valid_axis(axis) || packed == nullptr || n_iter < 0 || n_iter > 64 ||
+        !valid_flags(flags))
         return KVARN_EINVAL;
     if (!valid_bits(bits)) return KVARN_EUNSUPPORTED;
     const int st = check_tiles(x, n_tiles, tile_stride, token_stride, tile_offset);
@@ -81,14 +83,14 @@ int kvarn_quantize_tiles(const void* x, int x_dtype, int64_t n_tiles, int64_t ti
     if (dst_tile_index != nullptr && (reinterpret_cast<uintptr_t>(dst_tile_index) & 7u) != 0) return KVARN_EALIGN;
     if (n_tiles == 0) return KVARN_OK;
     QuantizeArgs a{x, x_dtype, n_tiles, tile_stride, token_stride, tile_offset, bits, axis, n_iter,
-                   static_cast<uint8_t*>(packed), dst_tile_index, stream};
+                   static_cast<uint8_t*>(packed), dst_tile_index, (flags & KVARN_NO_ROTATION) ? 0 : 1, stream};
     return hip_status(kvarn::launch_quantize(a));
 }
 
 int kvarn_dequantize_tiles(const void* packed, const int64_t* src_tile_index, int64_t n_tiles, int bits, int axis,
                            void* out, int out_dtype, int64_t tile_stride, int64_t token_stride,
-                           const int64_t* dst_tile_offset, hipStream_t stream) {
-    if (!valid_dtype(out_dtype) || !valid_axis(axis) || packed == nullptr) return KVARN_EINVAL;
+                           const int64_t* dst_tile_offset, int flags, hipStream_t stream) {
+    if (!valid_dtype(out_dtype) || !valid_axis(axis) || packed == nullptr || !valid_flags(flags)) return KVARN_EINVAL;
     if (!valid_bits(bits)) return KVARN_EUNSUPPORTED;
     const int st = check_tiles(out, n_tiles, tile_stride, token_stride, dst_tile_offset);
     if (st != KVARN_OK) return st;
@@ -96,7 +98,7 @@ int kvarn_dequantize_tiles(const void* packed, const int64_t* src_tile_index, in
     if (src_tile_index != nullptr && (reinterpret_cast<uintptr_t>(src_tile_index) & 7u) != 0) return KVARN_EALIGN;
     if (n_tiles == 0) return KVARN_OK;
     DequantizeArgs a{static_cast<const uint8_t*>(packed), src_tile_index, n_tiles, bits, axis, out, out_dtype,
-                     tile_stride, token_stride, dst_tile_offset, stream};
+                     tile_stride, token_stride, dst_tile_offset, (flags & KVARN_NO_ROTATION) ? 0 : 1, stream};
     return hip_status(kvarn::launch_dequantize(a));
 }
 
@@ -121,10 +123,10 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
 int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
                       const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
                       int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, void* out,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, size_t workspace_bytes, int flags, hipStream_t stream) {
     if (q == nullptr || k_packed == nullptr || v_packed == nullptr || n_tiles_per_seq == nullptr ||
         out == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0 || n_records < 0 ||
-        n_q_heads % n_kv_heads != 0 || !valid_sm_scale(sm_scale))
+        n_q_heads % n_kv_heads != 0 || !valid_sm_scale(sm_scale) || !valid_flags(flags))
         return KVARN_EINVAL;
     if (!valid_bits(bits_k) || !valid_bits(bits_v) || n_q_heads / n_kv_heads > 8) return KVARN_EUNSUPPORTED;
     if (batch > 65535 || n_kv_heads > 65535) return KVARN_EUNSUPPORTED;  // grid y/z limits
@@ -152,6 +154,7 @@ int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed,
     a.sm_scale = sm_scale;
     a.out = static_cast<uint16_t*>(out);
     a.workspace = static_cast<float*>(workspace);
+    a.rotate = (flags & KVARN_NO_ROTATION) ? 0 : 1;
     a.stream = stream;
     kvarn::decode_split_plan(batch, n_kv_heads, n_q_heads, max_tiles, &a.n_splits, &a.tiles_per_split);
     return hip_status(kvarn::launch_decode(a));

@@ -15,6 +15,7 @@ struct QuantizeArgs {
     int bits, axis, n_iter;
     uint8_t* packed;
     const int64_t* dst_index;
+    int rotate;                 // 0 with KVARN_NO_ROTATION
     hipStream_t stream;
 };
 
@@ -27,6 +28,7 @@ struct DequantizeArgs {
     int out_dtype;
     int64_t tile_stride, token_stride;
     const int64_t* dst_offset;
+    int rotate;
     hipStream_t stream;
 };
 
@@ -46,6 +48,7 @@ struct DecodeArgs {
     uint16_t* out;
     float* workspace;
     int n_splits, tiles_per_split;
+    int rotate;
     hipStream_t stream;
 };
 

@@ -58,6 +58,7 @@ namespace {
 
 constexpr float kInvN = 1.0f / 128.0f;
 constexpr float kInvNN = 1.0f / 16384.0f;
+constexpr float kSqrtN = 11.313708498984761f;       // sqrt(128)
 constexpr float kDegRel2 = 2.3283064365386963e-10f;  // (2^-16)^2: degenerate if var <= 2^-32 rms^2
 constexpr float kDegAbs2 = 7.52316384526264e-37f;    // 2^-120
 constexpr float kCancel = 16.0f;                     // mean^2 > 16 var: exact second pass
@@ -340,7 +341,7 @@ template <int BITS, int AXIS, int DT>
 __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
                                                           int64_t token_stride, const int64_t* __restrict__ tile_off,
                                                           int n_iter, uint8_t* __restrict__ packed,
-                                                          const int64_t* __restrict__ dst_index) {
+                                                          const int64_t* __restrict__ dst_index, int rotate) {
     using R = Rec<BITS>;
     __shared__ Smem sm;
 
@@ -348,9 +349,11 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
     const int rg = lane >> 4, cg = lane & 15, hl = lane >> 4;  // hl = (bit 5, bit 4) = rg
     // output channel group of this lane and the sign of its rotated values: the
     // 16-bit path rotates on the matrix cores in natural order, the fp32 path
-    // with the DPP network (permuted groups, known signs)
-    const int og = DT == kF32 ? out_group(cg) : cg;
-    const float sig = DT == kF32 ? mask_sign(kWhtSigma, cg) : 1.0f;
+    // with the DPP network (permuted groups, known signs); without the rotation
+    // the lane keeps its own channel group
+    const bool dpp_net = DT == kF32 && rotate;
+    const int og = dpp_net ? out_group(cg) : cg;
+    const float sig = dpp_net ? mask_sign(kWhtSigma, cg) : 1.0f;
     const int row0 = 32 * w + 8 * rg;                            // first token of this lane's block
     const int a_own = 4 * ((cg >> 3) & 1) + 2 * ((cg >> 2) & 1) + ((cg >> 1) & 1);  // row owned after row_rs
     const int jc0 = 2 * hl;                                      // first local column owned after col_rs
@@ -360,7 +363,16 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
     // ---- 1. load and rotate ------------------------------------------------------
     float y[8][8];
     const bool vec = ((start | token_stride) & 7) == 0;
-    if constexpr (DT == kF32) {
+    if (!rotate) {
+        // the variant without the rotation: y = sqrt(128) X keeps the scaling
+        // the normalisation below expects of an unnormalised rotation
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            load8<DT>(x, start + (int64_t)(row0 + a) * token_stride + 8 * cg, vec, y[a]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[a][j] *= kSqrtN;
+        }
+    } else if constexpr (DT == kF32) {
 #pragma unroll
         for (int a = 0; a < 8; ++a) load8<DT>(x, start + (int64_t)(row0 + a) * token_stride + 8 * cg, vec, y[a]);
         const float s1 = mask_sign(kWhtS1, cg), s2 = mask_sign(kWhtS2, cg);
@@ -695,17 +707,17 @@ hipError_t launch_bits_axis(const QuantizeArgs& a) {
     case kF16:
         quantize_kernel<BITS, AXIS, kF16><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
                                                                           a.tile_offset, a.n_iter, a.packed,
-                                                                          a.dst_index);
+                                                                          a.dst_index, a.rotate);
         break;
     case kBF16:
         quantize_kernel<BITS, AXIS, kBF16><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
                                                                            a.tile_offset, a.n_iter, a.packed,
-                                                                           a.dst_index);
+                                                                           a.dst_index, a.rotate);
         break;
     default:
         quantize_kernel<BITS, AXIS, kF32><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
                                                                           a.tile_offset, a.n_iter, a.packed,
-                                                                          a.dst_index);
+                                                                          a.dst_index, a.rotate);
         break;
     }
     return hipGetLastError();

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvarn.so
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 F16, BF16, F32 = 0, 1, 2
 AXIS_K, AXIS_V = 0, 1
+NO_ROTATION = 1          # flag: the variant without the Walsh-Hadamard rotation (KIVI with n_iter = 0)
 HEAD_DIM = TILE = 128
 
 # Every function declared in include/kvarn.h, with its ctypes signature.
@@ -26,10 +27,10 @@ SIGNATURES = {
     "kvarn_tile_bytes": (_SZ, [_I]),
     "kvarn_parse_preset": (_I, [ctypes.c_char_p, _P, _P, _P]),
     "kvarn_status_string": (ctypes.c_char_p, [_I]),
-    "kvarn_quantize_tiles": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _P, _P, _P]),
-    "kvarn_dequantize_tiles": (_I, [_P, _P, _I64, _I, _I, _P, _I, _I64, _I64, _P, _P]),
+    "kvarn_quantize_tiles": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _P, _P, _I, _P]),
+    "kvarn_dequantize_tiles": (_I, [_P, _P, _I64, _I, _I, _P, _I, _I64, _I64, _P, _I, _P]),
     "kvarn_decode_attn_workspace_bytes": (_SZ, [_I64, _I, _I, _I]),
-    "kvarn_decode_attn": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
+    "kvarn_decode_attn": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _I, _P]),
 }
 
 _lib = None
@@ -103,43 +104,45 @@ def _check(fn, st):
 def quantize_tiles(x: torch.Tensor, n_tiles: int, bits: int, axis: int, *, tile_stride: int = TILE * HEAD_DIM,
                    token_stride: int = HEAD_DIM, tile_offset: torch.Tensor | None = None,
                    out: torch.Tensor | None = None, dst_index: torch.Tensor | None = None, n_iter: int = 8,
-                   stream=None) -> torch.Tensor:
+                   flags: int = 0, stream=None) -> torch.Tensor:
     """Quantise tiles of ``x`` (fp16/bf16/fp32 on the GPU) into packed uint8 records [n, Pb]."""
     if out is None:
         out = torch.empty((n_tiles, tile_bytes(bits)), dtype=torch.uint8, device=x.device)
     st = load().kvarn_quantize_tiles(_ptr(x), _DT[x.dtype], n_tiles, tile_stride, token_stride, _ptr(tile_offset),
-                                     bits, axis, n_iter, _ptr(out), _ptr(dst_index), _stream(stream))
+                                     bits, axis, n_iter, _ptr(out), _ptr(dst_index), flags, _stream(stream))
     _check("kvarn_quantize_tiles", st)
     return out
 
 
-def quantize(x: torch.Tensor, bits: int, axis: int, n_iter: int = 8, stream=None) -> torch.Tensor:
+def quantize(x: torch.Tensor, bits: int, axis: int, n_iter: int = 8, flags: int = 0, stream=None) -> torch.Tensor:
     """Dense ``x[..., T, 128]`` (T a multiple of 128, contiguous) -> records [x.numel() / 16384, Pb]."""
     assert x.is_contiguous() and x.shape[-1] == HEAD_DIM and x.shape[-2] % TILE == 0
-    return quantize_tiles(x, x.numel() // (TILE * HEAD_DIM), bits, axis, n_iter=n_iter, stream=stream)
+    return quantize_tiles(x, x.numel() // (TILE * HEAD_DIM), bits, axis, n_iter=n_iter, flags=flags, stream=stream)
 
 
 def dequantize_tiles(packed: torch.Tensor, n_tiles: int, bits: int, axis: int, out: torch.Tensor, *,
                      tile_stride: int = TILE * HEAD_DIM, token_stride: int = HEAD_DIM,
                      src_index: torch.Tensor | None = None, dst_offset: torch.Tensor | None = None,
-                     stream=None) -> torch.Tensor:
+                     flags: int = 0, stream=None) -> torch.Tensor:
     st = load().kvarn_dequantize_tiles(_ptr(packed), _ptr(src_index), n_tiles, bits, axis, _ptr(out),
-                                       _DT[out.dtype], tile_stride, token_stride, _ptr(dst_offset), _stream(stream))
+                                       _DT[out.dtype], tile_stride, token_stride, _ptr(dst_offset), flags,
+                                       _stream(stream))
     _check("kvarn_dequantize_tiles", st)
     return out
 
 
-def dequantize(packed: torch.Tensor, bits: int, axis: int, dtype=torch.float32, stream=None) -> torch.Tensor:
+def dequantize(packed: torch.Tensor, bits: int, axis: int, dtype=torch.float32, flags: int = 0,
+               stream=None) -> torch.Tensor:
     """Records [n, Pb] -> tiles [n, 128, 128] of ``dtype``."""
     n = packed.shape[0]
     out = torch.empty((n, TILE, HEAD_DIM), dtype=dtype, device=packed.device)
-    return dequantize_tiles(packed, n, bits, axis, out, stream=stream)
+    return dequantize_tiles(packed, n, bits, axis, out, flags=flags, stream=stream)
 
 
 def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor, n_tiles_per_seq: torch.Tensor,
                 n_kv_heads: int, max_tiles: int, bits_k: int, bits_v: int, *, block_table: torch.Tensor | None = None,
                 sm_scale: float | None = None, out: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                workspace: torch.Tensor | None = None, flags: int = 0, stream=None) -> torch.Tensor:
     """q fp16 [batch][n_q_heads][128] -> attention output fp16 of the same shape."""
     batch, n_q_heads, _ = q.shape
     if sm_scale is None:
@@ -152,6 +155,7 @@ def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
     n_records = min(k_packed.shape[0], v_packed.shape[0])
     st = load().kvarn_decode_attn(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table), _ptr(n_tiles_per_seq),
                                   n_records, batch, n_q_heads, n_kv_heads, max_tiles, bits_k, bits_v,
-                                  float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+                                  float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(), flags,
+                                  _stream(stream))
     _check("kvarn_decode_attn", st)
     return out

@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.kvo_dequantize_tiles.restype = I
         L.kvo_dequantize_tiles.argtypes = [P, I64, I, I, I, P]
         L.kvo_decode_attn.restype = I
-        L.kvo_decode_attn.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, D, P]
+        L.kvo_decode_attn.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, P]
         L.kvo_num_threads.restype = I
         L.kvo_num_threads.argtypes = []
         _lib = L
@@ -209,7 +209,7 @@ def dequantize(records: np.ndarray, bits: int, axis: int, rotate: bool = True) -
 
 
 def decode_attn(q_f16_bits, k_records, v_records, n_tiles, n_q_heads, n_kv_heads, max_tiles, bits_k, bits_v,
-                sm_scale=None, block_table=None) -> np.ndarray:
+                sm_scale=None, block_table=None, rotate: bool = True) -> np.ndarray:
     """out[b][hq][128] float64; q_f16_bits: uint16 [b][hq][128]."""
     q = np.ascontiguousarray(q_f16_bits, np.uint16)
     batch = q.shape[0]
@@ -221,7 +221,7 @@ def decode_attn(q_f16_bits, k_records, v_records, n_tiles, n_q_heads, n_kv_heads
         sm_scale = 1.0 / np.sqrt(N)
     out = np.empty((batch, n_q_heads, N), np.float64)
     rc = lib().kvo_decode_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(nt), batch, n_q_heads, n_kv_heads,
-                               max_tiles, bits_k, bits_v, float(sm_scale), _ptr(out))
+                               max_tiles, bits_k, bits_v, int(rotate), float(sm_scale), _ptr(out))
     if rc != 0:
         raise ValueError("oracle decode_attn rejected its arguments")
     return out

@@ -637,13 +637,14 @@ int kvo_dequantize_tiles(const uint8_t *records, int64_t n_tiles, int bits, int 
  * tile j < min(n_tiles[b], max_tiles) is record
  *   idx = block_table ? block_table[row] : row,  row = (b * n_kv_heads + h) * max_tiles + j
  * of k_rec (K layout, bits_k) and v_rec (V layout, bits_v).  With the exact
- * (binary64) dequantised K and V tiles,
+ * (binary64) dequantised K and V tiles (dequantised with or without the
+ * inverse rotation, as the records were written),
  *   s_t = sm_scale * q . k_t,  p = softmax(s),  out = sum_t p_t v_t.
  * A sequence with no tiles gets a zero output.
  */
 int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_rec, const int32_t *block_table,
                     const int32_t *n_tiles, int64_t batch, int n_q_heads, int n_kv_heads, int max_tiles, int bits_k,
-                    int bits_v, double sm_scale, double *out)
+                    int bits_v, int rotate, double sm_scale, double *out)
 {
     if (batch < 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0 ||
         n_q_heads / n_kv_heads > 64 || max_tiles < 0 || kvo_record_bytes(bits_k) == 0 ||
@@ -673,7 +674,7 @@ int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_re
             for (int j = 0; j < nt; ++j) {
                 int64_t row = (b * n_kv_heads + kvh) * (int64_t)max_tiles + j;
                 int64_t idx = block_table ? block_table[row] : row;
-                dequant_one(k_rec + idx * pk, bits_k, AX_K, 1, h, kt);
+                dequant_one(k_rec + idx * pk, bits_k, AX_K, rotate, h, kt);
                 for (int t = 0; t < N; ++t)
                     for (int g = 0; g < gs; ++g) {
                         double acc = 0.0;
@@ -699,7 +700,7 @@ int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_re
             for (int j = 0; j < nt; ++j) {
                 int64_t row = (b * n_kv_heads + kvh) * (int64_t)max_tiles + j;
                 int64_t idx = block_table ? block_table[row] : row;
-                dequant_one(v_rec + idx * pv, bits_v, AX_V, 1, h, vt);
+                dequant_one(v_rec + idx * pv, bits_v, AX_V, rotate, h, vt);
                 for (int g = 0; g < gs; ++g)
                     for (int t = 0; t < N; ++t) {
                         double p = s[((size_t)g * nt + j) * N + t];

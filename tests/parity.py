@@ -62,11 +62,12 @@ class Report(dict):
         return ", ".join(f"{k}={v}" for k, v in self.items())
 
 
-def compare_quantize(view: "oracle.TileView", bits: int, axis: int, gpu_rec: np.ndarray, n_iter: int = 8) -> Report:
+def compare_quantize(view: "oracle.TileView", bits: int, axis: int, gpu_rec: np.ndarray, n_iter: int = 8,
+                     rotate: bool = True) -> Report:
     """Run the full protocol for the tiles of `view` against GPU records [n][Pb]."""
     gpu_rec = np.ascontiguousarray(gpu_rec, np.uint8)
     L = 2 ** bits - 1
-    ref_rec, dbg = oracle.quantize(view, bits, axis, n_iter=n_iter, debug=True)
+    ref_rec, dbg = oracle.quantize(view, bits, axis, n_iter=n_iter, rotate=rotate, debug=True)
     gc, g1, g2, gz = oracle.record_fields(gpu_rec, bits)
     rc, r1, r2, rz = oracle.record_fields(ref_rec, bits)
     rep = Report(tiles=view.n)
@@ -91,7 +92,7 @@ def compare_quantize(view: "oracle.TileView", bits: int, axis: int, gpu_rec: np.
     zmax = np.abs(zn).reshape(view.n, -1).max(1)[:, None]
 
     # 2. group scale and zero-point, given the GPU's s2
-    s1_pre, z_pre = oracle.group_meta_given_s2(view, bits, axis, g2)
+    s1_pre, z_pre = oracle.group_meta_given_s2(view, bits, axis, g2, rotate=rotate)
     s1_gpu = fp8_values(g1)
     z_gpu = gz.view(np.float16).astype(np.float64)
     ok1 = meta_ok(s1_gpu, s1_pre, "fp8", REL_META * s1_pre + 2 * ABS32 * zmax / L, floor=FP8_FLOOR)
@@ -102,7 +103,7 @@ def compare_quantize(view: "oracle.TileView", bits: int, axis: int, gpu_rec: np.
     rep["z_bad"] = int((~okz).sum())
 
     # 3. codes, given all of the GPU's metadata
-    codes_ref, t = oracle.codes_given_meta(view, bits, axis, gpu_rec)
+    codes_ref, t = oracle.codes_given_meta(view, bits, axis, gpu_rec, rotate=rotate)
     codes_gpu = oracle.unpack_codes(gpu_rec, bits, axis)
     diff = codes_gpu.astype(np.int64) - codes_ref.astype(np.int64)
     s1g = s1_gpu[:, None, :] if axis == 0 else s1_gpu[:, :, None]

@@ -43,8 +43,8 @@ def test_host_helpers():
     assert kvarn.status_string(kvarn.EALIGN) == "misaligned pointer or stride"
 
 
-def q(x=A, dt=kvarn.BF16, n=1, ts=16384, tok=128, off=None, bits=2, axis=0, it=8, out=A2, dst=None):
-    return kvarn.load().kvarn_quantize_tiles(x, dt, n, ts, tok, off, bits, axis, it, out, dst, None)
+def q(x=A, dt=kvarn.BF16, n=1, ts=16384, tok=128, off=None, bits=2, axis=0, it=8, out=A2, dst=None, fl=0):
+    return kvarn.load().kvarn_quantize_tiles(x, dt, n, ts, tok, off, bits, axis, it, out, dst, fl, None)
 
 
 def test_quantize_argument_errors():
@@ -61,11 +61,13 @@ def test_quantize_argument_errors():
     assert q(tok=132) == kvarn.EALIGN
     assert q(ts=16388) == kvarn.EALIGN
     assert q(off=P(0x10004)) == kvarn.EALIGN
+    assert q(fl=2) == kvarn.EINVAL and q(fl=-1) == kvarn.EINVAL  # unknown variant flags
     assert q(n=0) == kvarn.OK  # empty batch: a no-op that touches no device
+    assert q(n=0, fl=kvarn.NO_ROTATION, it=0) == kvarn.OK
 
 
-def dq(rec=A, src=None, n=1, bits=2, axis=1, out=A2, dt=kvarn.F32, ts=16384, tok=128, off=None):
-    return kvarn.load().kvarn_dequantize_tiles(rec, src, n, bits, axis, out, dt, ts, tok, off, None)
+def dq(rec=A, src=None, n=1, bits=2, axis=1, out=A2, dt=kvarn.F32, ts=16384, tok=128, off=None, fl=0):
+    return kvarn.load().kvarn_dequantize_tiles(rec, src, n, bits, axis, out, dt, ts, tok, off, fl, None)
 
 
 def test_dequantize_argument_errors():
@@ -76,12 +78,14 @@ def test_dequantize_argument_errors():
     assert dq(rec=MIS) == kvarn.EALIGN
     assert dq(src=P(0x10002)) == kvarn.EALIGN
     assert dq(tok=100) == kvarn.EINVAL
+    assert dq(fl=4) == kvarn.EINVAL
     assert dq(n=0) == kvarn.OK
+    assert dq(n=0, fl=kvarn.NO_ROTATION) == kvarn.OK
 
 
 def da(qp=A, k=A, v=A, bt=None, nt=A, nrec=10, b=2, hq=8, hkv=2, mt=4, bk=2, bv=2, out=A2, ws=A, wsb=1 << 20,
-       sm=0.088):
-    return kvarn.load().kvarn_decode_attn(qp, k, v, bt, nt, nrec, b, hq, hkv, mt, bk, bv, sm, out, ws, wsb, None)
+       sm=0.088, fl=0):
+    return kvarn.load().kvarn_decode_attn(qp, k, v, bt, nt, nrec, b, hq, hkv, mt, bk, bv, sm, out, ws, wsb, fl, None)
 
 
 def test_decode_argument_errors():
@@ -94,6 +98,8 @@ def test_decode_argument_errors():
     assert da(ws=None) == kvarn.EWORKSPACE
     assert da(wsb=16) == kvarn.EWORKSPACE
     assert da(b=0) == kvarn.OK
+    assert da(fl=8) == kvarn.EINVAL
+    assert da(b=0, fl=kvarn.NO_ROTATION) == kvarn.OK
     for sm in (float("nan"), float("inf"), 2.0 ** 33, -(2.0 ** 33), 2.0 ** -33):
         assert da(sm=sm) == kvarn.EINVAL, sm
     for sm in (0.0, -0.088, 2.0 ** 32, 2.0 ** -32):

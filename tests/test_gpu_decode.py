@@ -69,6 +69,30 @@ def test_decode_softmax_scales(dev, sm_scale):
     assert err.max() <= TOL
 
 
+@pytest.mark.parametrize("n_iter", [0, 8])
+def test_decode_without_rotation(dev, n_iter):
+    """KVARN_NO_ROTATION records (KIVI at n_iter = 0): attention in the channel
+    domain against the oracle's attention over the records dequantised without
+    the inverse rotation."""
+    batch, hkv, hq, max_tiles = 3, 2, 8, 3
+    rng = np.random.default_rng(51 + n_iter)
+    n_rec = batch * hkv * max_tiles
+    kx = (rng.standard_normal((n_rec, 128, 128)) * np.exp(rng.normal(0, 0.5, (n_rec, 1, 128)))).astype(np.float16)
+    vx = rng.standard_normal((n_rec, 128, 128)).astype(np.float16)
+    kr = oracle.quantize(oracle.TileView.dense(tiles_bits(kx), oracle.DT_F16), 2, K, n_iter=n_iter, rotate=False)
+    vr = oracle.quantize(oracle.TileView.dense(tiles_bits(vx), oracle.DT_F16), 2, V, n_iter=n_iter, rotate=False)
+    q = rng.standard_normal((batch, hq, 128)).astype(np.float16)
+    n_tiles = np.array([3, 2, 1], np.int32)
+    out = kvarn.decode_attn(torch.from_numpy(q).to(dev), torch.from_numpy(kr).to(dev), torch.from_numpy(vr).to(dev),
+                            torch.from_numpy(n_tiles).to(dev), hkv, max_tiles, 2, 2, flags=kvarn.NO_ROTATION)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    ref = oracle.decode_attn(q.view(np.uint16), kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2, rotate=False)
+    err = parity.rel_l2_rows(got, ref)
+    _log("no rotation", n_iter, "max rel l2", err.max())
+    assert err.max() <= TOL
+
+
 def test_decode_block_table_empty_and_out_of_range(dev):
     """Paged records through a block table; an empty sequence gives zeros; table
     entries outside the record buffer contribute nothing."""

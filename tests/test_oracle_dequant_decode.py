@@ -88,21 +88,21 @@ def test_roundtrip_reduces_error_vs_kivi(orc):
 
 
 # ----------------------------------------------------------------------------- decode attention
-def _cache(orc, n_seq, n_kv, n_tiles, seed, bits_k=2, bits_v=2, f=None):
+def _cache(orc, n_seq, n_kv, n_tiles, seed, bits_k=2, bits_v=2, f=None, n_iter=8, rotate=True):
     rng = np.random.default_rng(seed)
     kx = rng.standard_normal((n_seq * n_kv * n_tiles, N, N)).astype(np.float16)
     vx = rng.standard_normal((n_seq * n_kv * n_tiles, N, N)).astype(np.float16)
     if f is not None:
         kx, vx = f(kx, vx)
-    kr = orc.quantize(orc.TileView.dense(tiles_bits(kx), orc.DT_F16), bits_k, K)
-    vr = orc.quantize(orc.TileView.dense(tiles_bits(vx), orc.DT_F16), bits_v, V)
+    kr = orc.quantize(orc.TileView.dense(tiles_bits(kx), orc.DT_F16), bits_k, K, n_iter=n_iter, rotate=rotate)
+    vr = orc.quantize(orc.TileView.dense(tiles_bits(vx), orc.DT_F16), bits_v, V, n_iter=n_iter, rotate=rotate)
     return kr, vr
 
 
-def _brute(orc, q, kr, vr, n_tiles, hq, hkv, max_tiles, bk, bv, block_table=None):
+def _brute(orc, q, kr, vr, n_tiles, hq, hkv, max_tiles, bk, bv, block_table=None, rotate=True):
     """Decode attention from the oracle's own dequantised tiles with scipy's softmax."""
-    kd = orc.dequantize(kr, bk, K)
-    vd = orc.dequantize(vr, bv, V)
+    kd = orc.dequantize(kr, bk, K, rotate=rotate)
+    vd = orc.dequantize(vr, bv, V, rotate=rotate)
     gs = hq // hkv
     out = np.zeros((q.shape[0], hq, N))
     for b in range(q.shape[0]):
@@ -128,6 +128,22 @@ def test_decode_matches_brute_force_gqa_ragged(orc):
     got = orc.decode_attn(q.view(np.uint16), kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2)
     ref = _brute(orc, q, kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2)
     assert np.abs(got - ref).max() < 1e-12 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("n_iter", [0, 8])
+def test_decode_without_rotation_matches_brute_force(orc, n_iter):
+    """The variant without the rotation (KIVI when n_iter = 0): attention over the
+    channel-domain records equals scipy's softmax over the records dequantised
+    without the inverse rotation; with the rotation flag wrong it does not."""
+    n_seq, hkv, hq, max_tiles = 2, 2, 8, 2
+    kr, vr = _cache(orc, n_seq, hkv, max_tiles, seed=15, n_iter=n_iter, rotate=False)
+    q = np.random.default_rng(16).standard_normal((n_seq, hq, N)).astype(np.float16)
+    n_tiles = np.array([2, 1], np.int32)
+    got = orc.decode_attn(q.view(np.uint16), kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2, rotate=False)
+    ref = _brute(orc, q, kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2, rotate=False)
+    assert np.abs(got - ref).max() < 1e-12 * np.abs(ref).max()
+    wrong = orc.decode_attn(q.view(np.uint16), kr, vr, n_tiles, hq, hkv, max_tiles, 2, 2, rotate=True)
+    assert np.abs(wrong - ref).max() > 1e-2 * np.abs(ref).max()
 
 
 def test_decode_block_table_and_empty_sequence(orc):
