@@ -153,7 +153,66 @@ def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2):
             cold(lambda: kvarn.dequantize_tiles(rec, n, bits, axis, out, token_stride=ts, dst_offset=offs))  # noqa
     per_op["dequantize_cold"] = cold.mean_ms()
     del junk
-    return dict(n_tiles_per_cache=n, bits=bits, wall_s=wall, per_op_ms=per_op, record_bytes=pb)
+
+    # Method variants on the same K tiles: the method, Hadamard-only (no
+    # normalisation) and KIVI (no rotation, no normalisation).
+    variants = {}
+    for name, n_iter, flags in (("kvarn", 8, 0), ("hadamard_only", 0, 0), ("kivi", 0, kvarn.NO_ROTATION)):
+        tq, td = OpTimer(), OpTimer()
+        for i in range(max(4, steps // 10) + 2):
+            fq = lambda: kvarn.quantize_tiles(k, n, bits, kvarn.AXIS_K, token_stride=ts, tile_offset=offs,  # noqa
+                                              out=rk, n_iter=n_iter, flags=flags)
+            fd = lambda: kvarn.dequantize_tiles(rk, n, bits, kvarn.AXIS_K, ok, token_stride=ts,  # noqa
+                                                dst_offset=offs, flags=flags)
+            tq(fq) if i >= 2 else fq()
+            td(fd) if i >= 2 else fd()
+        variants[name] = {"n_iter": n_iter, "rotation": not flags, "quantize_k_ms": tq.mean_ms(),
+                          "dequantize_k_ms": td.mean_ms()}
+    return dict(n_tiles_per_cache=n, bits=bits, wall_s=wall, per_op_ms=per_op, record_bytes=pb, variants=variants)
+
+
+def bench_app_i(contexts=(4096, 8192, 16384, 32768), heads=16, reps=20):
+    """KVarN vs KIVI decode attention (fused dequantisation) at the shape of the
+    dequantisation-overhead measurement the pages report: 16 attention heads,
+    head_dim 128, groups of 128, 4k-32k tokens, one query token.  Each call is
+    timed as a HIP-graph replay of `reps` calls."""
+    dev = torch.device("cuda:0")
+    g = synth.generator(1006, dev)
+    rows = []
+    for T in contexts:
+        nt = T // 128
+        q, kx, vx = synth.decode_attn_layer(g, n_seq=1, n_kv_heads=heads, n_q_heads=heads, n_tokens=T, device=dev)
+        n_tiles = torch.full((1,), nt, dtype=torch.int32, device=dev)
+        row = {"tokens": T}
+        for name, n_iter, flags in (("kvarn", 8, 0), ("kivi", 0, kvarn.NO_ROTATION)):
+            kr = kvarn.quantize(kx, 2, kvarn.AXIS_K, n_iter=n_iter, flags=flags)
+            vr = kvarn.quantize(vx, 2, kvarn.AXIS_V, n_iter=n_iter, flags=flags)
+            ws = torch.empty(kvarn.workspace_bytes(1, heads, heads, nt), dtype=torch.uint8, device=dev)
+            out = torch.empty_like(q)
+            call = lambda: kvarn.decode_attn(q, kr, vr, n_tiles, heads, nt, 2, 2, out=out, workspace=ws,  # noqa
+                                             flags=flags)
+            call()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(reps):
+                    call()
+            times = []
+            for _ in range(7):
+                s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record()
+                graph.replay()
+                e0.record()
+                torch.cuda.synchronize()
+                times.append(s0.elapsed_time(e0) * 1e3 / reps)
+            row[f"{name}_us"] = float(np.median(times))
+            del graph
+        row["kvarn_over_kivi_pct"] = 100.0 * (row["kvarn_us"] / row["kivi_us"] - 1.0)
+        rows.append(row)
+    return {"what": "decode attention with fused dequantisation, KVarN records vs KIVI records (no rotation, "
+                    "no normalisation), 16 heads, head_dim 128, one query token, median time per call over "
+                    "HIP-graph replays",
+            "rows": rows}
 
 
 def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768, bits=2):
@@ -347,8 +406,10 @@ def main():
                      "algorithmic_bytes_per_launch": q_alg, "hbm_GBs": q_ach, "hbm_frac": q_ach / HBM_PEAK_GBS},
         "ops": ops,
     }
+    line["variants_decode_append_k"] = codec["variants"]
     if not args.no_decode:
         line["decode_attn"] = bench_decode(args.decode_passes, 2, layers=args.decode_layers)
+        line["dequant_overhead_vs_kivi"] = bench_app_i()
     if args.copy_calib:
         line["copy_reference"] = copy_reference()
     if not args.no_cpu_baseline:

@@ -246,6 +246,37 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const bool q_ok = 4 * chunk + qg < gs;
     WaveSmem& sm = smem[w];
 
+    // the query row first, then the first tile's loads, so that the query
+    // preparation below overlaps the first tile's memory latency
+    uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
+    if (q_ok) qraw = *reinterpret_cast<const uint4*>(q + ((b * n_q_heads + hq) * kN + 8 * n));
+
+    int nt = n_tiles_per_seq[b];
+    nt = nt < 0 ? 0 : (nt > max_tiles ? max_tiles : nt);
+    const int j0 = split * tiles_per_split;
+    const int j1 = min(j0 + tiles_per_split, nt);
+    const int64_t row_base = ((int64_t)b * n_kv_heads + kvh) * max_tiles;
+
+    // record index of tile j of this (sequence, KV head), or -1 when j is past the
+    // wave's range or the block-table entry is outside the record buffer
+    auto record_of = [&](int j) -> int64_t {
+        if (j >= j1) return -1;
+        const int64_t idx = block_table ? (int64_t)block_table[row_base + j] : row_base + j;
+        return (idx >= 0 && idx < n_records) ? idx : -1;    // uniform per wave
+    };
+    auto load = [&](int64_t idx, TileRaw& t) {
+        const bool ok = idx >= 0;
+        const __amdgpu_buffer_rsrc_t rk = record_rsrc(kp + (ok ? idx : 0) * RK::kBytes, ok ? RK::kBytes : 0);
+        const __amdgpu_buffer_rsrc_t rv = record_rsrc(vp + (ok ? idx : 0) * RV::kBytes, ok ? RV::kBytes : 0);
+        load_codes<BK>(rk, lane, t.kc);
+        load_codes<BV>(rv, lane, t.vc);
+        t.km = ld8(rk, RK::kS1 + 8 * lane);
+        t.vm = ld8(rv, RV::kS1 + 8 * lane);
+    };
+    TileRaw ta, tb;
+    int64_t ia = record_of(j0), ib;
+    load(ia, ta);
+
     // ---- rotated, scaled queries: lane holds channels 8*G..8*G+7 of query qg --
     // (without the rotation, KVARN_NO_ROTATION, the lane keeps channels 8n..)
     const int G = rotate ? out_group(n) : n;
@@ -254,8 +285,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     {
         float v[8];
         if (q_ok) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(q + ((b * n_q_heads + hq) * kN + 8 * n));
-            f16x8(raw, v);
+            f16x8(qraw, v);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = 0.0f;
@@ -309,29 +339,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 
-    int nt = n_tiles_per_seq[b];
-    nt = nt < 0 ? 0 : (nt > max_tiles ? max_tiles : nt);
-    const int j0 = split * tiles_per_split;
-    const int j1 = min(j0 + tiles_per_split, nt);
-    const int64_t row_base = ((int64_t)b * n_kv_heads + kvh) * max_tiles;
     const float e2 = pow2f((int)qexp);                  // 2^exponent of the query scaling
 
-    // record index of tile j of this (sequence, KV head), or -1 when j is past the
-    // wave's range or the block-table entry is outside the record buffer
-    auto record_of = [&](int j) -> int64_t {
-        if (j >= j1) return -1;
-        const int64_t idx = block_table ? (int64_t)block_table[row_base + j] : row_base + j;
-        return (idx >= 0 && idx < n_records) ? idx : -1;    // uniform per wave
-    };
-    auto load = [&](int64_t idx, TileRaw& t) {
-        const bool ok = idx >= 0;
-        const __amdgpu_buffer_rsrc_t rk = record_rsrc(kp + (ok ? idx : 0) * RK::kBytes, ok ? RK::kBytes : 0);
-        const __amdgpu_buffer_rsrc_t rv = record_rsrc(vp + (ok ? idx : 0) * RV::kBytes, ok ? RV::kBytes : 0);
-        load_codes<BK>(rk, lane, t.kc);
-        load_codes<BV>(rv, lane, t.vc);
-        t.km = ld8(rk, RK::kS1 + 8 * lane);
-        t.vm = ld8(rv, RV::kS1 + 8 * lane);
-    };
     auto compute = [&](const TileRaw& t) {
         // ---- metadata through LDS: each lane picks the scales of its channels / tokens
         sm.kmeta[lane] = t.km;
@@ -432,9 +441,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     // software pipeline: the next tile's loads are in flight while one is
     // computed; every iteration issues the same loads (tiles without a record
     // read zeros without touching memory) so the load counters stay exact.
-    TileRaw ta, tb;
-    int64_t ia = record_of(j0), ib;
-    load(ia, ta);
     for (int j = j0; j < j1; j += 2) {
         ib = record_of(j + 1);
         load(ib, tb);
