@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.kvo_dequantize_tiles.restype = I
         L.kvo_dequantize_tiles.argtypes = [P, I64, I, I, I, P]
         L.kvo_decode_attn.restype = I
-        L.kvo_decode_attn.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, P]
+        L.kvo_decode_attn.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, P, P, I, P, P, P, I, P]
         L.kvo_num_threads.restype = I
         L.kvo_num_threads.argtypes = []
         _lib = L
@@ -209,8 +209,11 @@ def dequantize(records: np.ndarray, bits: int, axis: int, rotate: bool = True) -
 
 
 def decode_attn(q_f16_bits, k_records, v_records, n_tiles, n_q_heads, n_kv_heads, max_tiles, bits_k, bits_v,
-                sm_scale=None, block_table=None, rotate: bool = True) -> np.ndarray:
-    """out[b][hq][128] float64; q_f16_bits: uint16 [b][hq][128]."""
+                sm_scale=None, block_table=None, rotate: bool = True, k_sink=None, v_sink=None, k_recent=None,
+                v_recent=None, n_recent=None) -> np.ndarray:
+    """out[b][hq][128] float64; q_f16_bits: uint16 [b][hq][128].  Optional FP16
+    windows as uint16 bits: k_sink / v_sink [b][n_kv_heads][n_sink][128],
+    k_recent / v_recent [b][n_kv_heads][recent_cap][128] with n_recent[b] valid."""
     q = np.ascontiguousarray(q_f16_bits, np.uint16)
     batch = q.shape[0]
     k = np.ascontiguousarray(k_records, np.uint8)
@@ -219,9 +222,19 @@ def decode_attn(q_f16_bits, k_records, v_records, n_tiles, n_q_heads, n_kv_heads
     bt = None if block_table is None else np.ascontiguousarray(block_table, np.int32)
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(N)
+    ks = vs = kr = vr = nr = None
+    n_sink = recent_cap = 0
+    if k_sink is not None:
+        ks, vs = np.ascontiguousarray(k_sink, np.uint16), np.ascontiguousarray(v_sink, np.uint16)
+        n_sink = ks.shape[2]
+    if k_recent is not None:
+        kr, vr = np.ascontiguousarray(k_recent, np.uint16), np.ascontiguousarray(v_recent, np.uint16)
+        nr = np.ascontiguousarray(n_recent, np.int32)
+        recent_cap = kr.shape[2]
     out = np.empty((batch, n_q_heads, N), np.float64)
     rc = lib().kvo_decode_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(nt), batch, n_q_heads, n_kv_heads,
-                               max_tiles, bits_k, bits_v, int(rotate), float(sm_scale), _ptr(out))
+                               max_tiles, bits_k, bits_v, int(rotate), float(sm_scale), _ptr(ks), _ptr(vs), n_sink,
+                               _ptr(kr), _ptr(vr), _ptr(nr), recent_cap, _ptr(out))
     if rc != 0:
         raise ValueError("oracle decode_attn rejected its arguments")
     return out

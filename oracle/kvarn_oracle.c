@@ -633,23 +633,34 @@ int kvo_dequantize_tiles(const uint8_t *records, int64_t n_tiles, int bits, int 
 
 /*
  * q[b][hq][128] FP16; out[b][hq][128] float64.  For sequence b and KV head
- * h = hq / (n_q_heads / n_kv_heads) (at most 64 query heads per KV head),
- * tile j < min(n_tiles[b], max_tiles) is record
- *   idx = block_table ? block_table[row] : row,  row = (b * n_kv_heads + h) * max_tiles + j
- * of k_rec (K layout, bits_k) and v_rec (V layout, bits_v).  With the exact
- * (binary64) dequantised K and V tiles (dequantised with or without the
- * inverse rotation, as the records were written),
- *   s_t = sm_scale * q . k_t,  p = softmax(s),  out = sum_t p_t v_t.
- * A sequence with no tiles gets a zero output.
+ * h = hq / (n_q_heads / n_kv_heads) (at most 64 query heads per KV head), the
+ * keys and values attended over are, in this order (the order does not change
+ * the result):
+ *   the n_sink FP16 sink tokens  k_sink[b][h][0 .. n_sink),
+ *   the packed body: tile j < min(n_tiles[b], max_tiles) is record
+ *     idx = block_table ? block_table[row] : row,  row = (b * n_kv_heads + h) * max_tiles + j
+ *     of k_rec (K layout, bits_k) and v_rec (V layout, bits_v), dequantised
+ *     exactly (binary64), with or without the inverse rotation as written,
+ *   the FP16 recent tokens  k_recent[b][h][0 .. min(n_recent[b], recent_cap)).
+ * The windows are the FP16 sink and trailing regions around the quantised body
+ * (paperlayer.ai summary, appendix D: S = 128, R = 128); NULL window pointers
+ * mean no window.  Then  s_t = sm_scale * q . k_t,  p = softmax(s),
+ * out = sum_t p_t v_t.  A sequence with no tokens gets a zero output.
  */
 int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_rec, const int32_t *block_table,
                     const int32_t *n_tiles, int64_t batch, int n_q_heads, int n_kv_heads, int max_tiles, int bits_k,
-                    int bits_v, int rotate, double sm_scale, double *out)
+                    int bits_v, int rotate, double sm_scale, const uint16_t *k_sink, const uint16_t *v_sink,
+                    int n_sink, const uint16_t *k_recent, const uint16_t *v_recent, const int32_t *n_recent,
+                    int recent_cap, double *out)
 {
     if (batch < 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0 ||
         n_q_heads / n_kv_heads > 64 || max_tiles < 0 || kvo_record_bytes(bits_k) == 0 ||
-        kvo_record_bytes(bits_v) == 0)
+        kvo_record_bytes(bits_v) == 0 || n_sink < 0 || recent_cap < 0)
         return -1;
+    if (k_sink == NULL || v_sink == NULL)
+        n_sink = 0;
+    if (k_recent == NULL || v_recent == NULL || n_recent == NULL)
+        recent_cap = 0;
     double h[NN];
     kvo_hadamard(h);
     const int gs = n_q_heads / n_kv_heads; /* query heads sharing one KV head */
@@ -658,62 +669,65 @@ int kvo_decode_attn(const uint16_t *q, const uint8_t *k_rec, const uint8_t *v_re
     for (int64_t b = 0; b < batch; ++b)
         for (int kvh = 0; kvh < n_kv_heads; ++kvh) {
             int nt = n_tiles[b] < max_tiles ? n_tiles[b] : max_tiles;
+            if (nt < 0)
+                nt = 0;
+            int nr = recent_cap > 0 ? n_recent[b] : 0;
+            nr = nr < 0 ? 0 : (nr > recent_cap ? recent_cap : nr);
+            const int64_t ntok = (int64_t)n_sink + (int64_t)nt * N + nr;
             double *o = out + (b * n_q_heads + (int64_t)kvh * gs) * N;
             for (int u = 0; u < gs * N; ++u)
                 o[u] = 0.0;
-            if (nt <= 0)
+            if (ntok == 0)
                 continue;
-            double *qd = (double *)malloc(sizeof(double) * gs * N);
-            double *kt = (double *)malloc(sizeof(double) * NN);
-            double *vt = (double *)malloc(sizeof(double) * NN);
-            double *s = (double *)malloc(sizeof(double) * (size_t)gs * nt * N);
-            for (int g = 0; g < gs; ++g)
-                for (int d = 0; d < N; ++d)
-                    qd[g * N + d] = kvo_f16_decode(q[(b * n_q_heads + (int64_t)kvh * gs + g) * N + d]);
-            /* scores s[g][token] = sm_scale * q_g . k_token */
-            for (int j = 0; j < nt; ++j) {
-                int64_t row = (b * n_kv_heads + kvh) * (int64_t)max_tiles + j;
-                int64_t idx = block_table ? block_table[row] : row;
-                dequant_one(k_rec + idx * pk, bits_k, AX_K, rotate, h, kt);
-                for (int t = 0; t < N; ++t)
-                    for (int g = 0; g < gs; ++g) {
-                        double acc = 0.0;
-                        for (int d = 0; d < N; ++d)
-                            acc += qd[g * N + d] * kt[t * N + d];
-                        s[((size_t)g * nt + j) * N + t] = sm_scale * acc;
-                    }
-            }
-            /* softmax over all tokens of the sequence, per query head */
-            double l[64];
-            for (int g = 0; g < gs; ++g) {
-                double *sg = s + (size_t)g * nt * N, m = -INFINITY;
-                for (int64_t u = 0; u < (int64_t)nt * N; ++u)
-                    if (sg[u] > m)
-                        m = sg[u];
-                l[g] = 0.0;
-                for (int64_t u = 0; u < (int64_t)nt * N; ++u) {
-                    sg[u] = exp(sg[u] - m);
-                    l[g] += sg[u];
+            double *kall = (double *)malloc(sizeof(double) * (size_t)ntok * N);
+            double *vall = (double *)malloc(sizeof(double) * (size_t)ntok * N);
+            double *s = (double *)malloc(sizeof(double) * (size_t)ntok);
+            int64_t u = 0;
+            for (int t = 0; t < n_sink; ++t, ++u)
+                for (int d = 0; d < N; ++d) {
+                    const int64_t e = (((int64_t)b * n_kv_heads + kvh) * n_sink + t) * N + d;
+                    kall[u * N + d] = kvo_f16_decode(k_sink[e]);
+                    vall[u * N + d] = kvo_f16_decode(v_sink[e]);
                 }
-            }
-            /* out[g] = sum_token p * v_token */
-            for (int j = 0; j < nt; ++j) {
+            for (int j = 0; j < nt; ++j, u += N) {
                 int64_t row = (b * n_kv_heads + kvh) * (int64_t)max_tiles + j;
                 int64_t idx = block_table ? block_table[row] : row;
-                dequant_one(v_rec + idx * pv, bits_v, AX_V, rotate, h, vt);
-                for (int g = 0; g < gs; ++g)
-                    for (int t = 0; t < N; ++t) {
-                        double p = s[((size_t)g * nt + j) * N + t];
-                        for (int d = 0; d < N; ++d)
-                            o[g * N + d] += p * vt[t * N + d];
-                    }
+                dequant_one(k_rec + idx * pk, bits_k, AX_K, rotate, h, kall + u * N);
+                dequant_one(v_rec + idx * pv, bits_v, AX_V, rotate, h, vall + u * N);
             }
-            for (int g = 0; g < gs; ++g)
+            for (int t = 0; t < nr; ++t, ++u)
+                for (int d = 0; d < N; ++d) {
+                    const int64_t e = (((int64_t)b * n_kv_heads + kvh) * recent_cap + t) * N + d;
+                    kall[u * N + d] = kvo_f16_decode(k_recent[e]);
+                    vall[u * N + d] = kvo_f16_decode(v_recent[e]);
+                }
+            for (int g = 0; g < gs; ++g) {
+                double qd[N];
                 for (int d = 0; d < N; ++d)
-                    o[g * N + d] /= l[g];
-            free(qd);
-            free(kt);
-            free(vt);
+                    qd[d] = kvo_f16_decode(q[(b * n_q_heads + (int64_t)kvh * gs + g) * N + d]);
+                /* scores, then softmax with the maximum subtracted */
+                double m = -INFINITY;
+                for (int64_t t = 0; t < ntok; ++t) {
+                    double acc = 0.0;
+                    for (int d = 0; d < N; ++d)
+                        acc += qd[d] * kall[t * N + d];
+                    s[t] = sm_scale * acc;
+                    if (s[t] > m)
+                        m = s[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < ntok; ++t) {
+                    s[t] = exp(s[t] - m);
+                    l += s[t];
+                }
+                for (int64_t t = 0; t < ntok; ++t)
+                    for (int d = 0; d < N; ++d)
+                        o[g * N + d] += s[t] * vall[t * N + d];
+                for (int d = 0; d < N; ++d)
+                    o[g * N + d] /= l;
+            }
+            free(kall);
+            free(vall);
             free(s);
         }
     return 0;

@@ -198,3 +198,73 @@ def test_rotated_domain_identity(orc):
     q = np.random.default_rng(15).standard_normal(N)
     h = hadamard_ref()
     assert np.allclose(yh @ (h @ q), xh @ q, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- FP16 windows
+def _windows(rng, n_seq, hkv, n_sink, cap):
+    ks = rng.standard_normal((n_seq, hkv, n_sink, N)).astype(np.float16)
+    vs = rng.standard_normal((n_seq, hkv, n_sink, N)).astype(np.float16)
+    kr = rng.standard_normal((n_seq, hkv, cap, N)).astype(np.float16)
+    vr = rng.standard_normal((n_seq, hkv, cap, N)).astype(np.float16)
+    return ks, vs, kr, vr
+
+
+def test_decode_windows_only_is_plain_attention(orc):
+    """With no packed tiles the decode oracle is plain attention (scipy softmax)
+    over the FP16 sink tokens and the valid recent tokens."""
+    n_seq, hkv, hq, n_sink, cap = 2, 2, 4, 5, 7
+    rng = np.random.default_rng(61)
+    ks, vs, kr, vr = _windows(rng, n_seq, hkv, n_sink, cap)
+    nrec = np.array([3, 0], np.int32)
+    q = rng.standard_normal((n_seq, hq, N)).astype(np.float16)
+    kb, vb = _cache(orc, n_seq, hkv, 1, seed=62)
+    got = orc.decode_attn(q.view(np.uint16), kb, vb, np.zeros(n_seq, np.int32), hq, hkv, 1, 2, 2,
+                          k_sink=ks.view(np.uint16), v_sink=vs.view(np.uint16), k_recent=kr.view(np.uint16),
+                          v_recent=vr.view(np.uint16), n_recent=nrec)
+    gs = hq // hkv
+    for b in range(n_seq):
+        for h in range(hq):
+            kk = np.concatenate([ks[b, h // gs], kr[b, h // gs, :nrec[b]]]).astype(np.float64)
+            vv = np.concatenate([vs[b, h // gs], vr[b, h // gs, :nrec[b]]]).astype(np.float64)
+            p = scipy.special.softmax(kk @ q[b, h].astype(np.float64) / np.sqrt(N))
+            assert np.allclose(got[b, h], p @ vv, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_windows_with_body_matches_brute_force(orc):
+    """Sink + packed body + ragged recent windows: the oracle equals scipy attention
+    over the concatenated tokens (body dequantised by the oracle), and is
+    unchanged when the sink and recent contents trade places."""
+    n_seq, hkv, hq, max_tiles, n_sink, cap = 2, 2, 8, 2, 4, 6
+    kb, vb = _cache(orc, n_seq, hkv, max_tiles, seed=63)
+    rng = np.random.default_rng(64)
+    ks, vs, kr, vr = _windows(rng, n_seq, hkv, n_sink, cap)
+    nrec = np.array([6, 2], np.int32)
+    nt = np.array([2, 1], np.int32)
+    q = rng.standard_normal((n_seq, hq, N)).astype(np.float16)
+    u16 = lambda a: a.view(np.uint16)  # noqa: E731
+    got = orc.decode_attn(q.view(np.uint16), kb, vb, nt, hq, hkv, max_tiles, 2, 2, k_sink=u16(ks), v_sink=u16(vs),
+                          k_recent=u16(kr), v_recent=u16(vr), n_recent=nrec)
+    kd = orc.dequantize(kb, 2, K)
+    vd = orc.dequantize(vb, 2, V)
+    gs = hq // hkv
+    for b in range(n_seq):
+        for h in range(hq):
+            kvh = h // gs
+            rows = [(b * hkv + kvh) * max_tiles + j for j in range(nt[b])]
+            kk = np.concatenate([ks[b, kvh].astype(np.float64), kd[rows].reshape(-1, N),
+                                 kr[b, kvh, :nrec[b]].astype(np.float64)])
+            vv = np.concatenate([vs[b, kvh].astype(np.float64), vd[rows].reshape(-1, N),
+                                 vr[b, kvh, :nrec[b]].astype(np.float64)])
+            p = scipy.special.softmax(kk @ q[b, h].astype(np.float64) / np.sqrt(N))
+            ref = p @ vv
+            assert np.abs(got[b, h] - ref).max() <= 1e-12 * np.abs(ref).max()
+    # the same tokens with the windows' roles exchanged (sink holds the first
+    # n_sink recent tokens when every recent count is at least n_sink)
+    nrec2 = np.array([n_sink, n_sink], np.int32)
+    a = orc.decode_attn(q.view(np.uint16), kb, vb, nt, hq, hkv, max_tiles, 2, 2, k_sink=u16(ks), v_sink=u16(vs),
+                        k_recent=u16(kr[:, :, :n_sink].copy()), v_recent=u16(vr[:, :, :n_sink].copy()),
+                        n_recent=nrec2)
+    c = orc.decode_attn(q.view(np.uint16), kb, vb, nt, hq, hkv, max_tiles, 2, 2,
+                        k_sink=u16(kr[:, :, :n_sink].copy()), v_sink=u16(vr[:, :, :n_sink].copy()),
+                        k_recent=u16(ks), v_recent=u16(vs), n_recent=nrec2)
+    assert np.abs(a - c).max() <= 1e-12 * np.abs(a).max()
