@@ -266,6 +266,38 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
     layer_ms = s.elapsed_time(e) / (passes * layers)
     if not torch.equal(out, ref):
         raise RuntimeError("decode attention: graph replay differs from the eager pass")
+    del graph
+
+    # The same layers with the pages' FP16 windows around the packed body: 128
+    # sink tokens and a trailing window of capacity 128 holding 1-128 tokens.
+    n_sink, cap = 128, 128
+    wins = []
+    for _ in range(layers):
+        w = [torch.randn((batch, hkv, n, 128), generator=g, device=dev).to(torch.float16)
+             for n in (n_sink, n_sink, cap, cap)]
+        wins.append(w)
+    n_recent = torch.randint(1, cap + 1, (batch,), generator=g, device=dev, dtype=torch.int32)
+
+    def window_pass():
+        for (q, kr, vr), (ks, vs, kt, vt) in zip(caches, wins):
+            kvarn.decode_attn(q, kr, vr, n_tiles, hkv, nt, bits, bits, out=out, workspace=ws, k_sink=ks, v_sink=vs,
+                              k_recent=kt, v_recent=vt, n_recent=n_recent)
+
+    window_pass()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        window_pass()
+    for _ in range(warmup):
+        graph.replay()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(passes):
+        graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    win_ms = s.elapsed_time(e) / (passes * layers)
+    del graph, wins
+    win_tokens = batch * (n_sink + float(n_recent.float().mean()))
     pb = kvarn.tile_bytes(bits)
     alg_bytes = 2 * batch * hkv * nt * pb + 2 * batch * hq * 128 * 2
     ach = alg_bytes / (layer_ms * 1e-3) / 1e9
@@ -281,6 +313,12 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode_mfma"),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "tokens_per_s": batch * hq / (layer_ms * 1e-3),
+        "with_fp16_windows": {
+            "layer_ms": win_ms, "sink_tokens": n_sink, "recent_capacity": cap,
+            "mean_recent_tokens": win_tokens / batch - n_sink,
+            "extra_bytes_per_layer": 2 * hkv * win_tokens * 256,
+            "note": "same layers, attention also over FP16 sink (128) and trailing (1-128) tokens per sequence",
+        },
     }
 
 

@@ -203,6 +203,35 @@ int kvarn_decode_attn(const void *q, const void *k_packed, const void *v_packed,
                       int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, void *out,
                       void *workspace, size_t workspace_bytes, int flags, hipStream_t stream);
 
+/*
+ * kvarn_decode_attn over a cache with FP16 windows around the packed body: the
+ * FP16 sink tokens and the FP16 trailing (most recent) tokens that the pages
+ * keep beside the quantised body (paperlayer.ai summary, appendix D: S = 128
+ * sink tokens, R = 128 trailing tokens, groups of G = 128; a trailing block is
+ * quantised into the body when it fills, pheeree.github.io blog, part 3).  The
+ * attention covers, for sequence b and KV head h, the sink tokens, the packed
+ * tiles (as in kvarn_decode_attn) and the valid recent tokens; attention does
+ * not depend on their order.  Arguments as for kvarn_decode_attn, plus:
+ *
+ *   k_sink, v_sink      device FP16 [batch][n_kv_heads][n_sink][128], or both
+ *                       NULL (no sink window); 16-byte aligned
+ *   n_sink              sink tokens per (sequence, KV head), 0 ... 65536
+ *   k_recent, v_recent  device FP16 [batch][n_kv_heads][recent_cap][128], or
+ *                       all three recent pointers NULL; 16-byte aligned
+ *   n_recent_per_seq    device int32[batch]: valid recent tokens of sequence b
+ *                       (clamped to [0, recent_cap]), 4-byte aligned
+ *   recent_cap          recent slots per (sequence, KV head), 0 ... 65536
+ *
+ * A window given with only some of its pointers is KVARN_EINVAL.  The window
+ * tokens are attended in fp32 from their FP16 values.
+ */
+int kvarn_decode_attn_windows(const void *q, const void *k_packed, const void *v_packed, const int32_t *block_table,
+                              const int32_t *n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
+                              int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale,
+                              const void *k_sink, const void *v_sink, int n_sink, const void *k_recent,
+                              const void *v_recent, const int32_t *n_recent_per_seq, int recent_cap, void *out,
+                              void *workspace, size_t workspace_bytes, int flags, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

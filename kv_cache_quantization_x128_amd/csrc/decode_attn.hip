@@ -213,6 +213,17 @@ __device__ __forceinline__ int piece_offset(int x0, int qg) {
     return stage_lane(16 * gl + 4 * qg) + s;
 }
 
+// FP16 sink and recent windows around the packed body (absent when the
+// pointers are null): k/v_sink [batch][n_kv_heads][n_sink][128],
+// k/v_recent [batch][n_kv_heads][recent_cap][128] with n_recent[b] valid.
+struct Windows {
+    const uint16_t *k_sink, *v_sink;
+    int n_sink;
+    const uint16_t *k_recent, *v_recent;
+    const int32_t* n_recent;
+    int recent_cap;
+};
+
 // Raw bytes of one K/V tile pair as one lane loads them.
 struct TileRaw {
     uint4 kc[8], vc[8];          // codes of record rows 8n + blk (lane group's 8 or 16 bytes)
@@ -230,7 +241,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ n_tiles_per_seq, int64_t n_records,
     int n_q_heads, int n_kv_heads, int max_tiles, int tiles_per_split, int n_splits, int gs, int n_chunks,
-    float scale_log2, float* __restrict__ ws, int rotate) {
+    float scale_log2, float* __restrict__ ws, int rotate, Windows win) {
     using RK = Rec<BK>;
     using RV = Rec<BV>;
     __shared__ WaveSmem smem[4];
@@ -450,6 +461,93 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         if (ib >= 0) compute(tb);
     }
 
+    // ---- FP16 sink and recent windows: this wave's share of their tokens, in
+    // the channel domain with the unrotated query (exact fp32 products), then
+    // moved into the rotated domain of acc.  Chunks of 8 tokens share one
+    // rescale of the running accumulators.
+    const int nr = win.k_recent ? min(max(win.n_recent[b], 0), win.recent_cap) : 0;
+    const int n_sink = win.k_sink ? win.n_sink : 0;
+    const int n_win = n_sink + nr;
+    if (n_win > 0) {
+        const int per = (n_win + n_splits - 1) / n_splits;
+        const int u0 = min(split * per, n_win), u1 = min(u0 + per, n_win);
+        if (u0 < u1) {                                   // uniform per wave
+            const int64_t hkv_row = (int64_t)b * n_kv_heads + kvh;
+            auto tok_ptr = [&](const uint16_t* sink, const uint16_t* recent, int u) -> const uint4* {
+                const uint16_t* p = u < n_sink ? sink + (hkv_row * n_sink + u) * kN
+                                               : recent + (hkv_row * win.recent_cap + (u - n_sink)) * kN;
+                return reinterpret_cast<const uint4*>(p + 8 * n);
+            };
+            float qp[8], accp[8];
+            f16x8(qraw, qp);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qp[i] *= scale_log2, accp[i] = 0.0f;
+            for (int c0 = u0; c0 < u1; c0 += 8) {
+                uint4 kr[8], vr[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int u = min(c0 + t, u1 - 1);  // slots past the range repeat a valid token, masked below
+                    kr[t] = *tok_ptr(win.k_sink, win.k_recent, u);
+                    vr[t] = *tok_ptr(win.v_sink, win.v_recent, u);
+                }
+                float sc[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    float kv[8];
+                    f16x8(kr[t], kv);
+                    float part = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) part = fmaf(qp[i], kv[i], part);
+                    sc[t] = c0 + t < u1 ? row_sum16(part) : -INFINITY;
+                }
+                float mt = sc[0];
+#pragma unroll
+                for (int t = 1; t < 8; ++t) mt = fmaxf(mt, sc[t]);
+                const float m_new = fmaxf(m_run, mt);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                float ps = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] *= alpha, accp[i] *= alpha;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float pt = __builtin_amdgcn_exp2f(sc[t] - m_new);
+                    float vv[8];
+                    f16x8(vr[t], vv);
+                    ps += pt;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) accp[i] = fmaf(pt, vv[i], accp[i]);
+                }
+                l_run = fmaf(l_run, alpha, ps);
+                m_run = m_new;
+            }
+            if (rotate) {
+                // accp H / sqrt(128): the query's 16-lane network leaves group
+                // out_group(n) (sign kWhtSigma) in lane n; acc's lane m holds
+                // group m, read from lane out_group(m)
+                fwht_regs<8>(accp);
+                const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
+                const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) accp[i] = fmaf(dpp<kDppXor1>(accp[i]), s1, accp[i]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) accp[i] = fmaf(dpp<kDppXor2>(accp[i]), s2, accp[i]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) accp[i] = fmaf(dpp<0x128>(accp[i]), s3, accp[i]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) accp[i] = fmaf(dpp<kDppHalfMirror>(accp[i]), s4, accp[i]);
+                const int src = 16 * qg + out_group(n);
+                const float sgn = mask_sign(kWhtSigma, out_group(n)) * kInvSqrtN;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[i] = fmaf(__int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(accp[i]))), sgn,
+                                  acc[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += accp[i];
+            }
+        }
+    }
+
     // ---- this wave's partial: m, l, acc[channels 8n..8n+7] of query qg
     if (q_ok) {
         float* dst = ws + ((b * n_q_heads + hq) * n_splits + split) * kPart;
@@ -541,7 +639,8 @@ hipError_t launch_bits(const DecodeArgs& a) {
     const dim3 grid((unsigned)((a.n_splits + 3) / 4), (unsigned)(a.n_kv_heads * n_chunks), (unsigned)a.batch);
     decode_mfma_kernel<BK, BV><<<grid, dim3(256), 0, a.stream>>>(
         a.q, a.k_packed, a.v_packed, a.block_table, a.n_tiles_per_seq, a.n_records, a.n_q_heads, a.n_kv_heads,
-        a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace, a.rotate);
+        a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace, a.rotate,
+        Windows{a.k_sink, a.v_sink, a.n_sink, a.k_recent, a.v_recent, a.n_recent, a.recent_cap});
     return hipGetLastError();
 }
 

@@ -120,19 +120,32 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
     return (size_t)batch * (size_t)n_q_heads * (size_t)n_splits * (size_t)kvarn::kDecodePart * sizeof(float);
 }
 
-int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
-                      const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
-                      int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, void* out,
-                      void* workspace, size_t workspace_bytes, int flags, hipStream_t stream) {
+int kvarn_decode_attn_windows(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
+                              const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
+                              int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale,
+                              const void* k_sink, const void* v_sink, int n_sink, const void* k_recent,
+                              const void* v_recent, const int32_t* n_recent_per_seq, int recent_cap, void* out,
+                              void* workspace, size_t workspace_bytes, int flags, hipStream_t stream) {
     if (q == nullptr || k_packed == nullptr || v_packed == nullptr || n_tiles_per_seq == nullptr ||
         out == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0 || n_records < 0 ||
         n_q_heads % n_kv_heads != 0 || !valid_sm_scale(sm_scale) || !valid_flags(flags))
+        return KVARN_EINVAL;
+    // windows: both pointers or neither; lengths in [0, 65536]
+    const bool has_sink = k_sink != nullptr || v_sink != nullptr;
+    const bool has_recent = k_recent != nullptr || v_recent != nullptr || n_recent_per_seq != nullptr;
+    if (has_sink && (k_sink == nullptr || v_sink == nullptr || n_sink < 0 || n_sink > 65536)) return KVARN_EINVAL;
+    if (has_recent && (k_recent == nullptr || v_recent == nullptr || n_recent_per_seq == nullptr || recent_cap < 0 ||
+                       recent_cap > 65536))
         return KVARN_EINVAL;
     if (!valid_bits(bits_k) || !valid_bits(bits_v) || n_q_heads / n_kv_heads > 8) return KVARN_EUNSUPPORTED;
     if (batch > 65535 || n_kv_heads > 65535) return KVARN_EUNSUPPORTED;  // grid y/z limits
     if (!aligned16(q) || !aligned16(k_packed) || !aligned16(v_packed) || !aligned16(out)) return KVARN_EALIGN;
     if ((reinterpret_cast<uintptr_t>(n_tiles_per_seq) & 3u) != 0 ||
         (block_table != nullptr && (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))
+        return KVARN_EALIGN;
+    if (has_sink && (!aligned16(k_sink) || !aligned16(v_sink))) return KVARN_EALIGN;
+    if (has_recent && (!aligned16(k_recent) || !aligned16(v_recent) ||
+                       (reinterpret_cast<uintptr_t>(n_recent_per_seq) & 3u) != 0))
         return KVARN_EALIGN;
     if (batch == 0) return KVARN_OK;
     const size_t need = kvarn_decode_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, max_tiles);
@@ -155,9 +168,25 @@ int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed,
     a.out = static_cast<uint16_t*>(out);
     a.workspace = static_cast<float*>(workspace);
     a.rotate = (flags & KVARN_NO_ROTATION) ? 0 : 1;
+    a.k_sink = has_sink && n_sink > 0 ? static_cast<const uint16_t*>(k_sink) : nullptr;
+    a.v_sink = has_sink && n_sink > 0 ? static_cast<const uint16_t*>(v_sink) : nullptr;
+    a.n_sink = has_sink ? n_sink : 0;
+    a.k_recent = has_recent && recent_cap > 0 ? static_cast<const uint16_t*>(k_recent) : nullptr;
+    a.v_recent = has_recent && recent_cap > 0 ? static_cast<const uint16_t*>(v_recent) : nullptr;
+    a.n_recent = has_recent && recent_cap > 0 ? n_recent_per_seq : nullptr;
+    a.recent_cap = has_recent ? recent_cap : 0;
     a.stream = stream;
     kvarn::decode_split_plan(batch, n_kv_heads, n_q_heads, max_tiles, &a.n_splits, &a.tiles_per_split);
     return hip_status(kvarn::launch_decode(a));
+}
+
+int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
+                      const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
+                      int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, void* out,
+                      void* workspace, size_t workspace_bytes, int flags, hipStream_t stream) {
+    return kvarn_decode_attn_windows(q, k_packed, v_packed, block_table, n_tiles_per_seq, n_records, batch, n_q_heads,
+                                     n_kv_heads, max_tiles, bits_k, bits_v, sm_scale, nullptr, nullptr, 0, nullptr,
+                                     nullptr, nullptr, 0, out, workspace, workspace_bytes, flags, stream);
 }
 
 }  // extern "C"

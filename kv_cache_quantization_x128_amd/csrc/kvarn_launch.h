@@ -49,6 +49,11 @@ struct DecodeArgs {
     float* workspace;
     int n_splits, tiles_per_split;
     int rotate;
+    const uint16_t *k_sink, *v_sink;        // FP16 windows (null: absent)
+    int n_sink;
+    const uint16_t *k_recent, *v_recent;
+    const int32_t* n_recent;
+    int recent_cap;
     hipStream_t stream;
 };
 

@@ -31,6 +31,8 @@ SIGNATURES = {
     "kvarn_dequantize_tiles": (_I, [_P, _P, _I64, _I, _I, _P, _I, _I64, _I64, _P, _I, _P]),
     "kvarn_decode_attn_workspace_bytes": (_SZ, [_I64, _I, _I, _I]),
     "kvarn_decode_attn": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _I, _P]),
+    "kvarn_decode_attn_windows": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _P,
+                                       _I, _P, _P, _SZ, _I, _P]),
 }
 
 _lib = None
@@ -142,8 +144,15 @@ def dequantize(packed: torch.Tensor, bits: int, axis: int, dtype=torch.float32, 
 def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor, n_tiles_per_seq: torch.Tensor,
                 n_kv_heads: int, max_tiles: int, bits_k: int, bits_v: int, *, block_table: torch.Tensor | None = None,
                 sm_scale: float | None = None, out: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None, flags: int = 0, stream=None) -> torch.Tensor:
-    """q fp16 [batch][n_q_heads][128] -> attention output fp16 of the same shape."""
+                workspace: torch.Tensor | None = None, flags: int = 0, k_sink: torch.Tensor | None = None,
+                v_sink: torch.Tensor | None = None, k_recent: torch.Tensor | None = None,
+                v_recent: torch.Tensor | None = None, n_recent: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """q fp16 [batch][n_q_heads][128] -> attention output fp16 of the same shape.
+
+    Optional FP16 windows around the packed body: k_sink / v_sink
+    [batch][n_kv_heads][n_sink][128]; k_recent / v_recent
+    [batch][n_kv_heads][recent_cap][128] with n_recent int32 [batch] valid tokens."""
     batch, n_q_heads, _ = q.shape
     if sm_scale is None:
         sm_scale = HEAD_DIM ** -0.5
@@ -153,9 +162,19 @@ def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     n_records = min(k_packed.shape[0], v_packed.shape[0])
-    st = load().kvarn_decode_attn(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table), _ptr(n_tiles_per_seq),
-                                  n_records, batch, n_q_heads, n_kv_heads, max_tiles, bits_k, bits_v,
-                                  float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(), flags,
-                                  _stream(stream))
-    _check("kvarn_decode_attn", st)
+    if k_sink is None and k_recent is None:
+        st = load().kvarn_decode_attn(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table),
+                                      _ptr(n_tiles_per_seq), n_records, batch, n_q_heads, n_kv_heads, max_tiles,
+                                      bits_k, bits_v, float(sm_scale), _ptr(out), _ptr(workspace),
+                                      workspace.numel(), flags, _stream(stream))
+        _check("kvarn_decode_attn", st)
+        return out
+    n_sink = 0 if k_sink is None else k_sink.shape[2]
+    cap = 0 if k_recent is None else k_recent.shape[2]
+    st = load().kvarn_decode_attn_windows(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table),
+                                          _ptr(n_tiles_per_seq), n_records, batch, n_q_heads, n_kv_heads, max_tiles,
+                                          bits_k, bits_v, float(sm_scale), _ptr(k_sink), _ptr(v_sink), n_sink,
+                                          _ptr(k_recent), _ptr(v_recent), _ptr(n_recent), cap, _ptr(out),
+                                          _ptr(workspace), workspace.numel(), flags, _stream(stream))
+    _check("kvarn_decode_attn_windows", st)
     return out

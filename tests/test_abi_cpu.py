@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     lib = kvarn.load()
     names = header_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(kvarn.SIGNATURES) == names
@@ -86,6 +86,22 @@ def test_dequantize_argument_errors():
 def da(qp=A, k=A, v=A, bt=None, nt=A, nrec=10, b=2, hq=8, hkv=2, mt=4, bk=2, bv=2, out=A2, ws=A, wsb=1 << 20,
        sm=0.088, fl=0):
     return kvarn.load().kvarn_decode_attn(qp, k, v, bt, nt, nrec, b, hq, hkv, mt, bk, bv, sm, out, ws, wsb, fl, None)
+
+
+def daw(ks=None, vs=None, ns=0, kr=None, vr=None, nr=None, cap=0, b=2):
+    return kvarn.load().kvarn_decode_attn_windows(A, A, A, None, A, 10, b, 8, 2, 4, 2, 2, 0.088, ks, vs, ns, kr, vr,
+                                                  nr, cap, A2, A, 1 << 20, 0, None)
+
+
+def test_decode_window_argument_errors():
+    assert daw(b=0) == kvarn.OK
+    assert daw(b=0, ks=A, vs=A, ns=128, kr=A, vr=A, nr=A, cap=128) == kvarn.OK
+    assert daw(ks=A) == kvarn.EINVAL                      # a sink window needs both pointers
+    assert daw(kr=A, vr=A) == kvarn.EINVAL                # a recent window needs its counts
+    assert daw(ks=A, vs=A, ns=-1) == kvarn.EINVAL
+    assert daw(kr=A, vr=A, nr=A, cap=65537) == kvarn.EINVAL
+    assert daw(ks=MIS, vs=A, ns=4) == kvarn.EALIGN
+    assert daw(kr=A, vr=A, nr=P(0x10002), cap=4) == kvarn.EALIGN
 
 
 def test_decode_argument_errors():

@@ -195,3 +195,59 @@ def test_decode_workspace_reuse_across_shapes(dev):
         torch.cuda.synchronize()
         _log("shape", (b, hq, hkv, mt), "max abs diff", (got.float() - want.float()).abs().max().item())
         assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("bk,bv,flags", [(2, 2, 0), (4, 2, 0), (2, 2, kvarn.NO_ROTATION)])
+def test_decode_with_fp16_windows(dev, bk, bv, flags):
+    """FP16 sink (S = 128) and trailing windows (capacity 128, ragged fill) around
+    a ragged packed body, against the oracle over the same three regions; one
+    sequence has an empty body, one an empty recent window."""
+    batch, hkv, hq, max_tiles, n_sink, cap = 3, 2, 8, 3, 128, 128
+    rng = np.random.default_rng(71 + bk + 8 * flags)
+    n_rec = batch * hkv * max_tiles
+    rot = not flags
+    kx = (rng.standard_normal((n_rec, 128, 128)) * np.exp(rng.normal(0, 0.5, (n_rec, 1, 128)))).astype(np.float16)
+    vx = rng.standard_normal((n_rec, 128, 128)).astype(np.float16)
+    kr = oracle.quantize(oracle.TileView.dense(tiles_bits(kx), oracle.DT_F16), bk, K, rotate=rot)
+    vr = oracle.quantize(oracle.TileView.dense(tiles_bits(vx), oracle.DT_F16), bv, V, rotate=rot)
+    ks = rng.standard_normal((batch, hkv, n_sink, 128)).astype(np.float16)
+    vs = rng.standard_normal((batch, hkv, n_sink, 128)).astype(np.float16)
+    kt = rng.standard_normal((batch, hkv, cap, 128)).astype(np.float16)
+    vt = rng.standard_normal((batch, hkv, cap, 128)).astype(np.float16)
+    n_recent = np.array([128, 37, 0], np.int32)
+    n_tiles = np.array([3, 0, 2], np.int32)
+    q = rng.standard_normal((batch, hq, 128)).astype(np.float16)
+    d = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    out = kvarn.decode_attn(d(q), d(kr), d(vr), d(n_tiles), hkv, max_tiles, bk, bv, flags=flags, k_sink=d(ks),
+                            v_sink=d(vs), k_recent=d(kt), v_recent=d(vt), n_recent=d(n_recent))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    u16 = lambda a: a.view(np.uint16)  # noqa: E731
+    ref = oracle.decode_attn(u16(q), kr, vr, n_tiles, hq, hkv, max_tiles, bk, bv, rotate=rot, k_sink=u16(ks),
+                             v_sink=u16(vs), k_recent=u16(kt), v_recent=u16(vt), n_recent=n_recent)
+    err = parity.rel_l2_rows(got, ref)
+    _log("windows", bk, bv, flags, "max rel l2", err.max())
+    assert err.max() <= TOL
+
+
+def test_decode_windows_only(dev):
+    """No packed tiles at all: plain attention over the FP16 windows."""
+    batch, hkv, hq, n_sink, cap = 2, 1, 4, 16, 8
+    rng = np.random.default_rng(81)
+    ks = rng.standard_normal((batch, hkv, n_sink, 128)).astype(np.float16)
+    vs = rng.standard_normal((batch, hkv, n_sink, 128)).astype(np.float16)
+    kt = rng.standard_normal((batch, hkv, cap, 128)).astype(np.float16)
+    vt = rng.standard_normal((batch, hkv, cap, 128)).astype(np.float16)
+    n_recent = np.array([8, 3], np.int32)
+    kr = np.zeros((1, kvarn.tile_bytes(2)), np.uint8)
+    q = rng.standard_normal((batch, hq, 128)).astype(np.float16)
+    d = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    out = kvarn.decode_attn(d(q), d(kr), d(kr), d(np.zeros(batch, np.int32)), hkv, 1, 2, 2, k_sink=d(ks),
+                            v_sink=d(vs), k_recent=d(kt), v_recent=d(vt), n_recent=d(n_recent))
+    torch.cuda.synchronize()
+    u16 = lambda a: a.view(np.uint16)  # noqa: E731
+    ref = oracle.decode_attn(u16(q), kr, kr, np.zeros(batch, np.int32), hq, hkv, 1, 2, 2, k_sink=u16(ks),
+                             v_sink=u16(vs), k_recent=u16(kt), v_recent=u16(vt), n_recent=n_recent)
+    err = parity.rel_l2_rows(out.float().cpu().numpy(), ref)
+    _log("windows only max rel l2", err.max())
+    assert err.max() <= TOL
