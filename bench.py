@@ -171,6 +171,56 @@ def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2):
     return dict(n_tiles_per_cache=n, bits=bits, wall_s=wall, per_op_ms=per_op, record_bytes=pb, variants=variants)
 
 
+def error_analysis(x: torch.Tensor, xd: torch.Tensor) -> dict:
+    """Error statistics of dequantised key vectors xd against the originals x
+    (rows = tokens, 128 channels), in float64.
+
+    Per token, the error splits exactly into a magnitude and a direction part
+    (pheeree.github.io blog, part 2, equation 3; paperlayer.ai summary, section 3
+    Methods, error decomposition):
+        |x - xd|^2 = (|x| - |xd|)^2 + 2 |x| |xd| (1 - cos theta) = E_M + E_D.
+    Reported: the relative MSE; the magnitude share E_M / E_T summed over the
+    tokens with the largest q of the errors (q = 50 % ... 0.1 %); the share of
+    the total squared error held by the largest 5 % of the entries (appendix C);
+    and the token-scale error |log2(|xd| / |x|)|, overall and for the 5 % of
+    tokens with the largest and the smallest norms (appendix B)."""
+    x, xd = x.double(), xd.double()
+    nk, nd = x.norm(dim=1), xd.norm(dim=1)
+    e_t = ((x - xd) ** 2).sum(1)
+    e_m = (nk - nd) ** 2
+    order = torch.argsort(e_t, descending=True)
+    shares = {}
+    for q in (0.5, 0.1, 0.05, 0.01, 0.001):
+        top = order[:max(1, int(round(q * e_t.numel())))]
+        shares[f"top_{q * 100:g}pct"] = float(e_m[top].sum() / e_t[top].sum())
+    el = ((x - xd) ** 2).reshape(-1)
+    k5 = max(1, int(round(0.05 * el.numel())))
+    scale = (torch.log2(nd.clamp_min(1e-300)) - torch.log2(nk.clamp_min(1e-300))).abs()
+    by_norm = torch.argsort(nk)
+    k = max(1, int(round(0.05 * nk.numel())))
+    return {"rel_mse": float(e_t.sum() / (x * x).sum()),
+            "magnitude_share": shares,
+            "top5pct_entries_share_of_sq_error": float(torch.topk(el, k5).values.sum() / el.sum()),
+            "token_scale_abs_log2": {"mean": float(scale.mean()), "largest_5pct_norms": float(scale[by_norm[-k:]].mean()),
+                                     "smallest_5pct_norms": float(scale[by_norm[:k]].mean())}}
+
+
+def bench_error_analysis(n_layers=4, bits=2):
+    """KVarN vs Hadamard-only vs KIVI on the keys of the decode-append workload
+    (first n_layers layers: 64 sequences x 8 KV heads, one 128-token tile each)."""
+    dev = torch.device("cuda:0")
+    k, _ = synth.decode_append(n_layers=n_layers, n_seq=64, n_heads=8, device=dev)
+    tiles = k.permute(0, 1, 3, 2, 4).contiguous()                        # [L][seq][head][128 tok][128 ch]
+    n = tiles.numel() // (128 * 128)
+    x = tiles.view(n * 128, 128).float()
+    out = {"workload": f"keys of the decode-append workload, {n} tiles ({n_layers} layers), {bits}-bit"}
+    for name, n_iter, flags in (("kvarn", 8, 0), ("hadamard_only", 0, 0), ("kivi", 0, kvarn.NO_ROTATION)):
+        rec = kvarn.quantize(tiles, bits, kvarn.AXIS_K, n_iter=n_iter, flags=flags)
+        xd = kvarn.dequantize(rec, bits, kvarn.AXIS_K, torch.float32, flags=flags).view(n * 128, 128)
+        out[name] = error_analysis(x, xd)
+    return out
+
+
 def bench_app_i(contexts=(4096, 8192, 16384, 32768), heads=16, reps=20):
     """KVarN vs KIVI decode attention (fused dequantisation) at the shape of the
     dequantisation-overhead measurement the pages report: 16 attention heads,
@@ -448,6 +498,7 @@ def main():
     if not args.no_decode:
         line["decode_attn"] = bench_decode(args.decode_passes, 2, layers=args.decode_layers)
         line["dequant_overhead_vs_kivi"] = bench_app_i()
+        line["error_analysis"] = bench_error_analysis()
     if args.copy_calib:
         line["copy_reference"] = copy_reference()
     if not args.no_cpu_baseline:
