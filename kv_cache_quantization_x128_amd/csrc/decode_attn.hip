@@ -236,12 +236,13 @@ struct WaveSmem {
     uint2 kmeta[64], vmeta[64];  // metadata blocks of the tile pair being computed
 };
 
-template <int BK, int BV>
+template <int BK, int BV, bool ROT>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ n_tiles_per_seq, int64_t n_records,
     int n_q_heads, int n_kv_heads, int max_tiles, int tiles_per_split, int n_splits, int gs, int n_chunks,
-    float scale_log2, float* __restrict__ ws, int rotate, Windows win) {
+    float scale_log2, float* __restrict__ ws, Windows win) {
+    constexpr bool rotate = ROT;   // false: KVARN_NO_ROTATION
     using RK = Rec<BK>;
     using RV = Rec<BV>;
     __shared__ WaveSmem smem[4];
@@ -561,9 +562,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
 // One wave per (sequence, KV head, chunk of 4 query heads): log-sum-exp merge
 // of the splits, inverse rotation (the same 16-lane Hadamard network as the
 // query rotation), FP16.  Lane = (query qg, channels 8n..8n+7).
+template <bool ROT>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws, int n_splits,
                                                             int n_q_heads, int n_kv_heads, int gs, int n_chunks,
-                                                            uint16_t* __restrict__ out, int rotate) {
+                                                            uint16_t* __restrict__ out) {
+    constexpr bool rotate = ROT;
     const int lane = threadIdx.x, qg = lane >> 4, n = lane & 15;
     const int chunk = blockIdx.x % n_chunks, kvh = (blockIdx.x / n_chunks) % n_kv_heads;
     const int64_t b = blockIdx.x / (n_chunks * n_kv_heads);
@@ -632,16 +635,25 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     }
 }
 
-template <int BK, int BV>
+template <int BK, int BV, bool ROT>
 hipError_t launch_bits(const DecodeArgs& a) {
     const int gs = a.n_q_heads / a.n_kv_heads;
     const int n_chunks = (gs + 3) / 4;
     const dim3 grid((unsigned)((a.n_splits + 3) / 4), (unsigned)(a.n_kv_heads * n_chunks), (unsigned)a.batch);
-    decode_mfma_kernel<BK, BV><<<grid, dim3(256), 0, a.stream>>>(
+    decode_mfma_kernel<BK, BV, ROT><<<grid, dim3(256), 0, a.stream>>>(
         a.q, a.k_packed, a.v_packed, a.block_table, a.n_tiles_per_seq, a.n_records, a.n_q_heads, a.n_kv_heads,
-        a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace, a.rotate,
+        a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace,
         Windows{a.k_sink, a.v_sink, a.n_sink, a.k_recent, a.v_recent, a.n_recent, a.recent_cap});
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const int n_groups = (int)(a.batch * a.n_kv_heads * n_chunks);
+    decode_combine_kernel<ROT><<<dim3((unsigned)n_groups), dim3(64), 0, a.stream>>>(
+        a.workspace, a.n_splits, a.n_q_heads, a.n_kv_heads, gs, n_chunks, a.out);
     return hipGetLastError();
+}
+
+template <int BK, int BV>
+hipError_t launch_bits(const DecodeArgs& a) {
+    return a.rotate ? launch_bits<BK, BV, true>(a) : launch_bits<BK, BV, false>(a);
 }
 
 }  // namespace
@@ -672,11 +684,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
         e = a.bits_v == 2 ? launch_bits<2, 2>(a) : launch_bits<2, 4>(a);
     else
         e = a.bits_v == 2 ? launch_bits<4, 2>(a) : launch_bits<4, 4>(a);
-    if (e != hipSuccess) return e;
-    const int gs = a.n_q_heads / a.n_kv_heads, n_chunks = (gs + 3) / 4;
-    decode_combine_kernel<<<dim3((unsigned)(a.batch * a.n_kv_heads * n_chunks)), dim3(64), 0, a.stream>>>(
-        a.workspace, a.n_splits, a.n_q_heads, a.n_kv_heads, gs, n_chunks, a.out, a.rotate);
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace kvarn

@@ -131,12 +131,12 @@ __device__ __forceinline__ void store_row8(void* __restrict__ out, int64_t e0, b
     }
 }
 
-template <int BITS, int AXIS, int ODT>
+template <int BITS, int AXIS, int ODT, bool ROT>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ packed,
                                                          const int64_t* __restrict__ src_index,
                                                          void* __restrict__ out, int64_t tile_stride,
-                                                         int64_t token_stride, const int64_t* __restrict__ dst_off,
-                                                         int rotate) {
+                                                         int64_t token_stride, const int64_t* __restrict__ dst_off) {
+    constexpr bool rotate = ROT;   // false: KVARN_NO_ROTATION
     using R = Rec<BITS>;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int rg = lane >> 4, cg = lane & 15;
@@ -225,24 +225,29 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
     for (int a = 0; a < 8; ++a) store_row8<ODT>(out, start + (int64_t)(row0 + a) * token_stride + 8 * og, vec, c[a]);
 }
 
-template <int BITS, int AXIS>
+template <int BITS, int AXIS, bool ROT>
 hipError_t launch_bits_axis(const DequantizeArgs& a) {
     const dim3 g((unsigned)a.n_tiles), block(256);
     switch (a.out_dtype) {
     case kF16:
-        dequantize_kernel<BITS, AXIS, kF16><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
-                                                                        a.token_stride, a.dst_offset, a.rotate);
+        dequantize_kernel<BITS, AXIS, kF16, ROT><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
+                                                                        a.token_stride, a.dst_offset);
         break;
     case kBF16:
-        dequantize_kernel<BITS, AXIS, kBF16><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
-                                                                         a.token_stride, a.dst_offset, a.rotate);
+        dequantize_kernel<BITS, AXIS, kBF16, ROT><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
+                                                                         a.token_stride, a.dst_offset);
         break;
     default:
-        dequantize_kernel<BITS, AXIS, kF32><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
-                                                                        a.token_stride, a.dst_offset, a.rotate);
+        dequantize_kernel<BITS, AXIS, kF32, ROT><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
+                                                                        a.token_stride, a.dst_offset);
         break;
     }
     return hipGetLastError();
+}
+
+template <int BITS, int AXIS>
+hipError_t launch_bits_axis(const DequantizeArgs& a) {
+    return a.rotate ? launch_bits_axis<BITS, AXIS, true>(a) : launch_bits_axis<BITS, AXIS, false>(a);
 }
 
 }  // namespace

@@ -337,11 +337,12 @@ __device__ __forceinline__ void row_bcast(Smem& sm, int w, int rg, int a_own, fl
 // 128 registers per lane, and the third workgroup hides the reduction and
 // barrier latencies of the other two.  The few long-lived addresses that no
 // longer fit are spilled once before the normalisation and reloaded after it.
-template <int BITS, int AXIS, int DT>
+template <int BITS, int AXIS, int DT, bool ROT>
 __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
                                                           int64_t token_stride, const int64_t* __restrict__ tile_off,
                                                           int n_iter, uint8_t* __restrict__ packed,
-                                                          const int64_t* __restrict__ dst_index, int rotate) {
+                                                          const int64_t* __restrict__ dst_index) {
+    constexpr bool rotate = ROT;   // false: KVARN_NO_ROTATION
     using R = Rec<BITS>;
     __shared__ Smem sm;
 
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
     // ---- 1. load and rotate ------------------------------------------------------
     float y[8][8];
     const bool vec = ((start | token_stride) & 7) == 0;
-    if (!rotate) {
+    if constexpr (!rotate) {
         // the variant without the rotation: y = sqrt(128) X keeps the scaling
         // the normalisation below expects of an unnormalised rotation
 #pragma unroll
@@ -700,27 +701,32 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
     }
 }
 
-template <int BITS, int AXIS>
+template <int BITS, int AXIS, bool ROT>
 hipError_t launch_bits_axis(const QuantizeArgs& a) {
     const dim3 grid((unsigned)a.n_tiles), block(256);
     switch (a.x_dtype) {
     case kF16:
-        quantize_kernel<BITS, AXIS, kF16><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
-                                                                          a.tile_offset, a.n_iter, a.packed,
-                                                                          a.dst_index, a.rotate);
+        quantize_kernel<BITS, AXIS, kF16, ROT><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
+                                                                               a.tile_offset, a.n_iter, a.packed,
+                                                                               a.dst_index);
         break;
     case kBF16:
-        quantize_kernel<BITS, AXIS, kBF16><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
-                                                                           a.tile_offset, a.n_iter, a.packed,
-                                                                           a.dst_index, a.rotate);
+        quantize_kernel<BITS, AXIS, kBF16, ROT><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
+                                                                                a.tile_offset, a.n_iter, a.packed,
+                                                                                a.dst_index);
         break;
     default:
-        quantize_kernel<BITS, AXIS, kF32><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
-                                                                          a.tile_offset, a.n_iter, a.packed,
-                                                                          a.dst_index, a.rotate);
+        quantize_kernel<BITS, AXIS, kF32, ROT><<<grid, block, 0, a.stream>>>(a.x, a.tile_stride, a.token_stride,
+                                                                               a.tile_offset, a.n_iter, a.packed,
+                                                                               a.dst_index);
         break;
     }
     return hipGetLastError();
+}
+
+template <int BITS, int AXIS>
+hipError_t launch_bits_axis(const QuantizeArgs& a) {
+    return a.rotate ? launch_bits_axis<BITS, AXIS, true>(a) : launch_bits_axis<BITS, AXIS, false>(a);
 }
 
 }  // namespace
