@@ -18,7 +18,10 @@
 // into the per-lane metadata) are chosen so that every output lane holds its
 // values with a positive sign, lane cg ending with output channel group
 // out_group(cg).  Each lane then writes 8 tokens x 8 channels as 16- or 32-byte
-// row segments.
+// row segments.  This vector path serves V records and records without the
+// rotation; K records with the rotation take the matrix-core kernel further
+// down (dequantize_k_mfma_kernel), whose contraction runs over the record's own
+// positions.
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
 
