@@ -98,7 +98,7 @@ class OpTimer:
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
 
 
-def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2):
+def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2, with_variants=True):
     dev = torch.device("cuda:0")
     log(f"generating decode-append inputs {layers}x{seqs}x128x{heads}x128 bf16")
     k, v = synth.decode_append(n_layers=layers, n_seq=seqs, n_heads=heads, device=dev)
@@ -158,6 +158,8 @@ def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2):
     # normalisation) and KIVI (no rotation, no normalisation).
     variants = {}
     for name, n_iter, flags in (("kvarn", 8, 0), ("hadamard_only", 0, 0), ("kivi", 0, kvarn.NO_ROTATION)):
+        if not with_variants:
+            break
         tq, td = OpTimer(), OpTimer()
         for i in range(max(4, steps // 10) + 2):
             fq = lambda: kvarn.quantize_tiles(k, n, bits, kvarn.AXIS_K, token_stride=ts, tile_offset=offs,  # noqa
@@ -265,7 +267,7 @@ def bench_app_i(contexts=(4096, 8192, 16384, 32768), heads=16, reps=20):
             "rows": rows}
 
 
-def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768, bits=2):
+def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768, bits=2, with_windows=True):
     dev = torch.device("cuda:0")
     nt = tokens // 128
     g = synth.generator(1005, dev)
@@ -318,6 +320,25 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
         raise RuntimeError("decode attention: graph replay differs from the eager pass")
     del graph
 
+    pb = kvarn.tile_bytes(bits)
+    alg_bytes = 2 * batch * hkv * nt * pb + 2 * batch * hq * 128 * 2
+    ach = alg_bytes / (layer_ms * 1e-3) / 1e9
+    res = {
+        "workload": f"decode attention: batch {batch}, {hq} query heads on {hkv} KV heads, head_dim 128, "
+                    f"{tokens}-token {bits}-bit K/V cache, {layers} layers",
+        "layer_ms": layer_ms,
+        "timing": f"HIP events around {passes} replays of a HIP graph holding the {layers}-layer pass",
+        "eager_layer_ms": eager_ms,
+        "eager_wall_s_per_pass": wall / passes,
+        "fp16_equiv_GBs": 2 * batch * hkv * nt * TILE_F16_BYTES / (layer_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode_mfma"),
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "tokens_per_s": batch * hq / (layer_ms * 1e-3),
+    }
+    if not with_windows:
+        return res
+
     # The same layers with the pages' FP16 windows around the packed body: 128
     # sink tokens and a trailing window of capacity 128 holding 1-128 tokens.
     n_sink, cap = 128, 128
@@ -348,28 +369,13 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
     win_ms = s.elapsed_time(e) / (passes * layers)
     del graph, wins
     win_tokens = batch * (n_sink + float(n_recent.float().mean()))
-    pb = kvarn.tile_bytes(bits)
-    alg_bytes = 2 * batch * hkv * nt * pb + 2 * batch * hq * 128 * 2
-    ach = alg_bytes / (layer_ms * 1e-3) / 1e9
-    return {
-        "workload": f"decode attention: batch {batch}, {hq} query heads on {hkv} KV heads, head_dim 128, "
-                    f"{tokens}-token {bits}-bit K/V cache, {layers} layers",
-        "layer_ms": layer_ms,
-        "timing": f"HIP events around {passes} replays of a HIP graph holding the {layers}-layer pass",
-        "eager_layer_ms": eager_ms,
-        "eager_wall_s_per_pass": wall / passes,
-        "fp16_equiv_GBs": 2 * batch * hkv * nt * TILE_F16_BYTES / (layer_ms * 1e-3) / 1e9,
-        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode_mfma"),
-                     "algorithmic_bytes_per_launch": alg_bytes},
-        "tokens_per_s": batch * hq / (layer_ms * 1e-3),
-        "with_fp16_windows": {
-            "layer_ms": win_ms, "sink_tokens": n_sink, "recent_capacity": cap,
-            "mean_recent_tokens": win_tokens / batch - n_sink,
-            "extra_bytes_per_layer": 2 * hkv * win_tokens * 256,
-            "note": "same layers, attention also over FP16 sink (128) and trailing (1-128) tokens per sequence",
-        },
+    res["with_fp16_windows"] = {
+        "layer_ms": win_ms, "sink_tokens": n_sink, "recent_capacity": cap,
+        "mean_recent_tokens": win_tokens / batch - n_sink,
+        "extra_bytes_per_layer": 2 * hkv * win_tokens * 256,
+        "note": "same layers, attention also over FP16 sink (128) and trailing (1-128) tokens per sequence",
     }
+    return res
 
 
 def copy_reference(reps=10, nbytes=1 << 28):
@@ -429,6 +435,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true", help="also time a plain 256 MiB device copy")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the method variants, the FP16-window decode, the KIVI comparison and the error "
+                         "analysis (counter runs: every dispatch of a kernel is then the headline workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the codec has no cross-GPU step); got --gpus {args.gpus}",
@@ -437,7 +446,7 @@ def main():
     kvarn.load()
     torch.cuda.init()
 
-    codec = bench_codec(args.steps, args.warmup)
+    codec = bench_codec(args.steps, args.warmup, with_variants=not args.no_extras)
     n = codec["n_tiles_per_cache"]
     per_op = codec["per_op_ms"]
     step_ms = codec["wall_s"] / args.steps * 1e3
@@ -494,11 +503,14 @@ def main():
                      "algorithmic_bytes_per_launch": q_alg, "hbm_GBs": q_ach, "hbm_frac": q_ach / HBM_PEAK_GBS},
         "ops": ops,
     }
-    line["variants_decode_append_k"] = codec["variants"]
+    if not args.no_extras:
+        line["variants_decode_append_k"] = codec["variants"]
     if not args.no_decode:
-        line["decode_attn"] = bench_decode(args.decode_passes, 2, layers=args.decode_layers)
-        line["dequant_overhead_vs_kivi"] = bench_app_i()
-        line["error_analysis"] = bench_error_analysis()
+        line["decode_attn"] = bench_decode(args.decode_passes, 2, layers=args.decode_layers,
+                                           with_windows=not args.no_extras)
+        if not args.no_extras:
+            line["dequant_overhead_vs_kivi"] = bench_app_i()
+            line["error_analysis"] = bench_error_analysis()
     if args.copy_calib:
         line["copy_reference"] = copy_reference()
     if not args.no_cpu_baseline:

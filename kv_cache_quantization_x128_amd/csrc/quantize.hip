@@ -455,8 +455,10 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
     float last_rvar = 0.0f, last_rms2r = 0.0f;
     int buf = 0;
 
-    for (int it = 0; it < n_iter; ++it) {
-        // channel step: moments of wr_i * y_ij over the 128 tokens
+    // Channel step: moments of wr_i * y_ij over the 128 tokens.  Returns the
+    // centred variances of the lane's two owned columns and the mean square of
+    // the matrix of this step.
+    auto channel_moments = [&](bool first, float (&var)[2], float& rms2) {
         float t[4];
         {
             float v[16];
@@ -475,10 +477,10 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             cross_wave<OpSum, OpSum>(sm, buf, w, lane, z, t);
             buf ^= 1;
         }
-        if (it == 0) colsq[0] = t[1], colsq[1] = t[3];
-        const float rms2 = wave_sum(t[1] + t[3]) * kInvNN;
+        if (first) colsq[0] = t[1], colsq[1] = t[3];
+        rms2 = wave_sum(t[1] + t[3]) * kInvNN;
         float mean[2] = {t[0] * kInvN, t[2] * kInvN};
-        float var[2] = {fmaf(-mean[0], mean[0], t[1] * kInvN), fmaf(-mean[1], mean[1], t[3] * kInvN)};
+        var[0] = fmaf(-mean[0], mean[0], t[1] * kInvN), var[1] = fmaf(-mean[1], mean[1], t[3] * kInvN);
         if (wave_any(mean[0] * mean[0] > kCancel * var[0] || mean[1] * mean[1] > kCancel * var[1])) {
             // exact centred second pass (uniform: every wave holds the same totals)
             float m8[8], unused[8];
@@ -500,6 +502,13 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             buf ^= 1;
             var[0] = t2[1] * kInvN, var[1] = t2[3] * kInvN;
         }
+    };
+    // The final channel step of V stands after the loop (its token step is absorbed
+    // into s1), so that the loop has no exit in the middle.
+    const int n_full = (AXIS == kAxisV && n_iter > 0) ? n_iter - 1 : n_iter;
+    for (int it = 0; it < n_full; ++it) {
+        float var[2], rms2;
+        channel_moments(it == 0, var, rms2);
         // degenerate rule on the stored scale (std floor 2^-60 * sqrt(128))
         const float thr = kDegRel2 * rms2, floor2 = kDegAbs2 * 128.0f;
         const bool rms_ok = rms2 >= floor2;
@@ -507,13 +516,6 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         float f[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) f[k] = step_factor(var[k], thr, floor2, fb);
-        if (AXIS == kAxisV && it == n_iter - 1) {
-            // c of the owned columns, unscaled: sqrt(var / 128) or rms / sqrt(128)
-#pragma unroll
-            for (int k = 0; k < 2; ++k)
-                gc[k] = (var[k] > thr && var[k] >= floor2) ? sqrtf(var[k] * kInvN) : (rms_ok ? sqrtf(rms2 * kInvN) : 1.0f);
-            break;   // the final token step of V is absorbed into s1
-        }
         col_bcast(sm, w, cg, hl, make_float4(sig * f[0], f[0] * f[0], sig * f[1], f[1] * f[1]), wc, wc2);
         // rms of the token-step matrix: sum_j colsq_j * wc_j^2 / 128^2 (wave-local)
         const float rms2r = wave_sum(fmaf(colsq[0], f[0] * f[0], colsq[1] * (f[1] * f[1]))) * kInvNN;
@@ -558,6 +560,16 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         const float fr = step_factor(rvar, kDegRel2 * rms2r, kDegAbs2, fbr);
         last_rvar = rvar, last_rms2r = rms2r;
         row_bcast(sm, w, rg, a_own, fr, fr * fr, wr, wr2);
+    }
+    if (AXIS == kAxisV && n_iter > 0) {
+        float var[2], rms2;
+        channel_moments(n_iter == 1, var, rms2);
+        const float thr = kDegRel2 * rms2, floor2 = kDegAbs2 * 128.0f;
+        const bool rms_ok = rms2 >= floor2;
+        // c of the owned columns, unscaled: sqrt(var / 128) or rms / sqrt(128)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            gc[k] = (var[k] > thr && var[k] >= floor2) ? sqrtf(var[k] * kInvN) : (rms_ok ? sqrtf(rms2 * kInvN) : 1.0f);
     }
     if (AXIS == kAxisK && n_iter > 0)   // r of the owned row after the last token step
         gr = (last_rvar > kDegRel2 * last_rms2r && last_rvar >= kDegAbs2)
