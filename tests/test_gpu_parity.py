@@ -152,12 +152,15 @@ def test_iteration_counts(dev, n_iter):
     parity.assert_quantize_parity(rep)
 
 
-def test_addressing_offsets_index_and_misalignment(dev):
+@pytest.mark.parametrize("axis", [K, V])
+def test_addressing_offsets_index_and_misalignment(dev, axis):
     """Tile offsets (including ones that are not 8-element aligned), a permuted
-    destination index and strided tokens give the same records as dense tiles."""
+    destination index and strided tokens give the same records as dense tiles,
+    and dequantising back through the same layout (the unaligned stores of both
+    the vector and the matrix-core dequantiser) gives the dense dequantisation."""
     rng = np.random.default_rng(9)
     dense = rng.standard_normal((5, 128, 128)).astype(np.float16)
-    ref = _gpu_quantize_dense(torch.from_numpy(dense).to(dev), 2, V)
+    ref = _gpu_quantize_dense(torch.from_numpy(dense).to(dev), 2, axis)
     token_stride = 136                                         # padded rows
     buf = np.zeros(6 * 128 * token_stride + 64, np.float16)
     offs = np.array([0, 128 * token_stride + 3, 2 * 128 * token_stride + 8,
@@ -167,20 +170,50 @@ def test_addressing_offsets_index_and_misalignment(dev):
             buf[o + t * token_stride: o + t * token_stride + 128] = dense[i, t]
     perm = np.array([3, 0, 4, 1, 2], np.int64)
     out = torch.zeros((5, kvarn.tile_bytes(2)), dtype=torch.uint8, device=dev)
-    kvarn.quantize_tiles(torch.from_numpy(buf).to(dev), 5, 2, V, token_stride=token_stride,
+    kvarn.quantize_tiles(torch.from_numpy(buf).to(dev), 5, 2, axis, token_stride=token_stride,
                          tile_offset=torch.from_numpy(offs).to(dev), out=out,
                          dst_index=torch.from_numpy(perm).to(dev))
     got = out.cpu().numpy()
     assert np.array_equal(got[perm], ref)
     # and back through the same strided layout
     back = torch.zeros(buf.shape, dtype=torch.float16, device=dev)
-    kvarn.dequantize_tiles(out, 5, 2, V, back, token_stride=token_stride,
+    kvarn.dequantize_tiles(out, 5, 2, axis, back, token_stride=token_stride,
                            src_index=torch.from_numpy(perm).to(dev), dst_offset=torch.from_numpy(offs).to(dev))
-    deq = kvarn.dequantize(torch.from_numpy(ref).to(dev), 2, V, torch.float16).cpu().numpy()
+    deq = kvarn.dequantize(torch.from_numpy(ref).to(dev), 2, axis, torch.float16).cpu().numpy()
     b = back.cpu().numpy()
     for i, o in enumerate(offs):
-        for t in (0, 77, 127):
+        for t in range(128):
             assert np.array_equal(b[o + t * token_stride: o + t * token_stride + 128], deq[i, t])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16, torch.float32])
+def test_dequantize_unaligned_outputs_match_aligned(dev, bits, axis, out_dtype):
+    """Dequantising into a padded token stride at tile offsets that are not
+    multiples of 8 elements (the element-wise store path) writes exactly what the
+    aligned vector stores write, for every output type, both record kinds and
+    both bit widths."""
+    rng = np.random.default_rng(31 + bits + 2 * axis)
+    x = torch.from_numpy(rng.standard_normal((3, 128, 128)).astype(np.float16)).to(dev)
+    rec = kvarn.quantize(x, bits, axis)
+    ref = kvarn.dequantize(rec, bits, axis, out_dtype)
+    ts = 136
+    offs = torch.tensor([1, 128 * ts + 3, 2 * 128 * ts + 7], dtype=torch.int64, device=dev)
+    buf = torch.full((3 * 128 * ts + 16,), 7.0, dtype=out_dtype, device=dev)
+    kvarn.dequantize_tiles(rec, 3, bits, axis, buf, token_stride=ts, dst_offset=offs)
+    torch.cuda.synchronize()
+    for i in range(3):
+        o = int(offs[i])
+        got = torch.stack([buf[o + t * ts: o + t * ts + 128] for t in range(128)])
+        assert torch.equal(got, ref[i])
+    # nothing outside the tiles' rows was touched
+    mask = torch.ones_like(buf, dtype=torch.bool)
+    for i in range(3):
+        o = int(offs[i])
+        for t in range(128):
+            mask[o + t * ts: o + t * ts + 128] = False
+    assert bool((buf[mask] == 7.0).all())
 
 
 def test_empty_batch_is_noop(dev):
