@@ -121,6 +121,39 @@ def compare_quantize(view: "oracle.TileView", bits: int, axis: int, gpu_rec: np.
     return rep
 
 
+_SUMMED = ("s2_equal", "s2_flips", "s2_bad", "s1_flips", "z_flips", "s1_bad", "z_bad", "code_ties", "code_bad",
+           "records_identical", "unexplained")
+
+
+def compare_quantize_many(tiles: np.ndarray, dtype: int, bits: int, axis: int, gpu_rec: np.ndarray,
+                          n_iter: int = 8, rotate: bool = True, chunk: int = 512) -> Report:
+    """compare_quantize for many dense tiles [n][128][128] (16-bit bits or
+    float32).  A record byte-identical to the oracle's passes every step of the
+    protocol trivially, so only the records that differ go through it (in chunks
+    of at most `chunk` tiles); the counts are those of the full protocol."""
+    gpu_rec = np.ascontiguousarray(gpu_rec, np.uint8)
+    tiles = np.ascontiguousarray(tiles).reshape(-1, N, N)
+    n = tiles.shape[0]
+    ref = oracle.quantize(oracle.TileView.dense(tiles, dtype), bits, axis, n_iter=n_iter, rotate=rotate)
+    same = (gpu_rec == ref).all(1)
+    rep = Report(tiles=n, full_protocol_tiles=int((~same).sum()))
+    for k in _SUMMED:
+        rep[k] = 0
+    rep["s2_equal"] = N * int(same.sum())
+    rep["records_identical"] = int(same.sum())
+    identical_codes = float(same.sum()) * N * N
+    diff = np.flatnonzero(~same)
+    for c0 in range(0, diff.size, chunk):
+        idx = diff[c0:c0 + chunk]
+        sub = compare_quantize(oracle.TileView.dense(tiles[idx], dtype), bits, axis, gpu_rec[idx], n_iter=n_iter,
+                               rotate=rotate)
+        for k in _SUMMED:
+            rep[k] += sub[k]
+        identical_codes += sub["raw_identical_codes"] * idx.size * N * N
+    rep["raw_identical_codes"] = identical_codes / (n * N * N) if n else 1.0
+    return rep
+
+
 def assert_quantize_parity(rep: Report, min_identical: float = 0.9999):
     assert rep["unexplained"] == 0, str(rep)
     assert rep["raw_identical_codes"] >= min_identical, str(rep)

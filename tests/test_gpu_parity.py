@@ -233,25 +233,38 @@ def _sample_dense(x_flat, offsets, idx, token_stride):
     return x_flat[o[:, None, None] + t[None]]
 
 
-def _check_sample(x_flat, offsets, token_stride, rec, bits, axis, n_sample, seed):
-    n = offsets.numel()
-    idx = torch.from_numpy(np.random.default_rng(seed).choice(n, size=min(n, n_sample), replace=False)).to(
-        offsets.device)
-    tiles = _sample_dense(x_flat, offsets, idx, token_stride)
-    view = oracle.TileView.dense(parity.bits_of(tiles), oracle.DT_BF16)
-    gpu = rec[idx].cpu().numpy()
-    rep = parity.compare_quantize(view, bits, axis, gpu)
-    _log(rep)
-    parity.assert_quantize_parity(rep)
-    # dequantise the sample on the GPU (fp32) against the oracle
-    out = kvarn.dequantize(rec[idx].contiguous(), bits, axis, torch.float32).cpu().numpy()
-    assert parity.dequant_fp32_error(out, oracle.dequantize(gpu, bits, axis)) < 1e-3
+def _check_tiles(x_flat, offsets, token_stride, rec, bits, axis, idx, tag, chunk=4096, n_deq=256):
+    """Quantise parity (the full protocol, fast path for byte-identical records)
+    of the tiles idx, gathered chunk by chunk from the GPU input at their exact
+    bytes, and the fp32 dequantisation of n_deq tiles per chunk."""
+    total = None
+    deq_err = 0.0
+    for c0 in range(0, idx.numel(), chunk):
+        ci = idx[c0:c0 + chunk]
+        tiles = parity.bits_of(_sample_dense(x_flat, offsets, ci, token_stride))
+        gpu = rec[ci].cpu().numpy()
+        rep = parity.compare_quantize_many(tiles, oracle.DT_BF16, bits, axis, gpu)
+        if total is None:
+            total = rep
+        else:
+            n_before = total["tiles"]
+            for k in parity._SUMMED + ("tiles", "full_protocol_tiles"):
+                total[k] += rep[k]
+            total["raw_identical_codes"] = (total["raw_identical_codes"] * n_before +
+                                            rep["raw_identical_codes"] * rep["tiles"]) / total["tiles"]
+        d = ci[torch.linspace(0, ci.numel() - 1, min(n_deq, ci.numel()), device=ci.device).long()]
+        out = kvarn.dequantize(rec[d].contiguous(), bits, axis, torch.float32).cpu().numpy()
+        deq_err = max(deq_err, parity.dequant_fp32_error(out, oracle.dequantize(rec[d].cpu().numpy(), bits, axis)))
+        _log(tag, f"tiles {c0 + ci.numel()}/{idx.numel()}", rep)
+    _log(tag, "total", total, "dequant max err / tile rms", deq_err)
+    parity.assert_quantize_parity(total)
+    assert deq_err < 1e-3
 
 
 def test_decode_append_full_size(dev):
     """36 layers x 64 sequences x 8 KV heads, one new 128-token block each, bf16,
-    token-major [layer][seq][token][head][128]; every tile quantised, 1024 sampled
-    per cache checked against the oracle; a second run is byte-identical."""
+    token-major [layer][seq][token][head][128]; every tile quantised and every
+    tile checked against the oracle; a second run is byte-identical."""
     L_, B_, H_ = 36, 64, 8
     k, v = synth.decode_append(n_layers=L_, n_seq=B_, n_heads=H_, device=dev)
     offs = synth.decode_append_offsets(L_, B_, H_, device=dev)
@@ -263,7 +276,7 @@ def test_decode_append_full_size(dev):
         rec2 = kvarn.quantize_tiles(x, n, 2, axis, token_stride=ts, tile_offset=offs)
         torch.cuda.synchronize()
         assert torch.equal(rec, rec2)
-        _check_sample(x.view(-1), offs, ts, rec, 2, axis, 1024, seed=5 + axis)
+        _check_tiles(x.view(-1), offs, ts, rec, 2, axis, torch.arange(n, device=dev), f"decode_append {name}")
         # round trip into the same strided layout
         back = torch.empty_like(x)
         kvarn.dequantize_tiles(rec, n, 2, axis, back, token_stride=ts, dst_offset=offs)
@@ -274,26 +287,38 @@ def test_decode_append_full_size(dev):
     torch.cuda.empty_cache()
 
 
-def test_prefill_full_size(dev):
-    """36 layers x 8 KV heads x 32768 tokens (bf16): all 147456 tiles, 512 sampled per cache."""
+@pytest.mark.parametrize("axis", [K, V])
+def test_prefill_full_size(dev, axis):
+    """36 layers x 8 KV heads x 32768 tokens (bf16): all 147456 tiles of the
+    cache quantised and every one checked against the oracle."""
     k, v = synth.prefill(device=dev)
-    for name, x, axis in (("K", k, K), ("V", v, V)):
-        _log("prefill", name)
-        rec = kvarn.quantize(x, 2, axis)
-        offs = torch.arange(rec.shape[0], device=dev, dtype=torch.int64) * 16384
-        _check_sample(x.view(-1), offs, 128, rec, 2, axis, 512, seed=11 + axis)
+    x = k if axis == K else v
     del k, v
+    name = "K" if axis == K else "V"
+    _log("prefill", name)
+    rec = kvarn.quantize(x, 2, axis)
+    offs = torch.arange(rec.shape[0], device=dev, dtype=torch.int64) * 16384
+    _check_tiles(x.view(-1), offs, 128, rec, 2, axis, torch.arange(rec.shape[0], device=dev), "prefill " + name)
+    del x, rec
     torch.cuda.empty_cache()
 
 
 def test_phi4_full_size(dev):
-    """Phi-4-14B shape: 40 layers x 10 KV heads x 8 sequences x 16384 tokens, 4-bit K, 2-bit V."""
+    """Phi-4-14B shape: 40 layers x 10 KV heads x 8 sequences x 16384 tokens,
+    4-bit K, 2-bit V.  Checked against the oracle: a seeded sample of 8192
+    tiles over layer, head and sequence, and every tile of one (layer, head)."""
     k, v = synth.phi4(device=dev)
+    per_head = 8 * 16384 // 128                       # tiles of one (layer, head)
     for name, x, axis, bits in (("K", k, K, 4), ("V", v, V, 2)):
         _log("phi4", name)
         rec = kvarn.quantize(x, bits, axis)
-        offs = torch.arange(rec.shape[0], device=dev, dtype=torch.int64) * 16384
-        _check_sample(x.view(-1), offs, 128, rec, bits, axis, 512, seed=21 + axis)
+        n = rec.shape[0]
+        offs = torch.arange(n, device=dev, dtype=torch.int64) * 16384
+        rng = np.random.default_rng(21 + axis)
+        sample = rng.choice(n, size=8192, replace=False)
+        one = (17 * 10 + 3) * per_head + np.arange(per_head)   # layer 17, head 3
+        idx = torch.from_numpy(np.unique(np.concatenate([sample, one]))).to(dev)
+        _check_tiles(x.view(-1), offs, 128, rec, bits, axis, idx, "phi4 " + name)
         del rec
     del k, v
     torch.cuda.empty_cache()

@@ -61,3 +61,25 @@ def test_planted_mistakes_are_flagged(case, name):
     bad = _corrupt(rec, locals()[name])
     rep = parity.compare_quantize(view, 2, 0, bad)
     assert rep["unexplained"] > 0, (name, str(rep))
+
+
+def test_many_tile_path_equals_full_protocol():
+    """compare_quantize_many (full protocol only for records that differ from the
+    oracle's) reports exactly what the full protocol reports, with planted
+    mistakes in a few of the tiles and identical records elsewhere."""
+    k, _ = synth.tiny()
+    tiles = tiles_bits(k)
+    rec = oracle.quantize(oracle.TileView.dense(tiles, oracle.DT_F16), 2, 0)
+    bad = rec.copy()
+    bad[1, 3 * 32] ^= 0x2          # a code two levels off
+    bad[5, 2048 * 2 + 7] ^= 0x1    # an s1 byte one FP8 step off
+    bad[6, 700] ^= 0x10            # another code
+    full = parity.compare_quantize(oracle.TileView.dense(tiles, oracle.DT_F16), 2, 0, bad)
+    many = parity.compare_quantize_many(tiles, oracle.DT_F16, 2, 0, bad, chunk=2)
+    assert many["full_protocol_tiles"] == 3
+    for key in parity._SUMMED:
+        assert many[key] == full[key], key
+    assert abs(many["raw_identical_codes"] - full["raw_identical_codes"]) < 1e-15
+    assert many["unexplained"] > 0
+    same = parity.compare_quantize_many(tiles, oracle.DT_F16, 2, 0, rec)
+    assert same["full_protocol_tiles"] == 0 and same["unexplained"] == 0 and same["raw_identical_codes"] == 1.0
