@@ -14,6 +14,9 @@ algorithmic HBM rate (tiles x (32768 + 4608) bytes) is reported beside it.
 Decode attention over the 2-bit cache (batch 16, 32 query heads on 8 KV heads,
 32768 tokens, 36 layers) is timed in the same run and reported in its own object.
 The oracle's quantise + dequantise is timed on a bounded sample on the host.
+Also in the line: the combined quantise + dequantise rate, a plain 256 MiB copy
+timed in the same run (the achievable-bandwidth reference), and the method
+variants on the K tiles (n_iter = 4 as a sensitivity row, Hadamard-only, KIVI).
 """
 from __future__ import annotations
 
@@ -157,7 +160,8 @@ def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2, with_variant
     # Method variants on the same K tiles: the method, Hadamard-only (no
     # normalisation) and KIVI (no rotation, no normalisation).
     variants = {}
-    for name, n_iter, flags in (("kvarn", 8, 0), ("hadamard_only", 0, 0), ("kivi", 0, kvarn.NO_ROTATION)):
+    for name, n_iter, flags in (("kvarn", 8, 0), ("kvarn_n_iter_4", 4, 0), ("hadamard_only", 0, 0),
+                                ("kivi", 0, kvarn.NO_ROTATION)):
         if not with_variants:
             break
         tq, td = OpTimer(), OpTimer()
@@ -419,8 +423,16 @@ def cpu_baseline(target_s=15.0, bits=2):
     if n_layers > 1:
         buf, offs = tiles(n_layers)
     dt = run(buf, offs, m)
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": 2 * m * TILE_F16_BYTES / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "cpus_in_affinity_mask": len(os.sched_getaffinity(0)),
             "sample": f"{m} K tiles ({n_layers} layers) of the decode-append workload, quantise + dequantise, "
                       f"{dt:.1f} s on the host"}
 
@@ -434,7 +446,8 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=36)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calib", action="store_true", help="also time a plain 256 MiB device copy")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="time the plain 256 MiB device copy 10 times instead of 5 (counter calibration runs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the method variants, the FP16-window decode, the KIVI comparison and the error "
                          "analysis (counter runs: every dispatch of a kernel is then the headline workload's)")
@@ -473,6 +486,9 @@ def main():
                        "fp16_equiv_GBs": n * TILE_F16_BYTES / (dq_ms * 1e-3) / 1e9,
                        "traffic": measured_traffic("dequantize"),
                        "note": "inside the step: records written by the preceding quantise launches"},
+        "combined": {"what": "quantise + dequantise of the same tiles: algorithmic bytes of both over the sum of "
+                             "their launch times", "GBs": 2 * q_alg / ((q_ms + dq_ms) * 1e-3) / 1e9,
+                     "frac_hbm": 2 * q_alg / ((q_ms + dq_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "dequantize_cold": {"launch_ms": dqc_ms, "tiles_per_s": n / (dqc_ms * 1e-3),
                             "algorithmic_GBs": q_alg / (dqc_ms * 1e-3) / 1e9,
                             "frac_hbm": q_alg / (dqc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -511,8 +527,7 @@ def main():
         if not args.no_extras:
             line["dequant_overhead_vs_kivi"] = bench_app_i()
             line["error_analysis"] = bench_error_analysis()
-    if args.copy_calib:
-        line["copy_reference"] = copy_reference()
+    line["copy_reference"] = copy_reference(reps=10 if args.copy_calib else 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
