@@ -52,6 +52,25 @@ def test_decode_small_gqa_bits_ragged(dev, gs, bk, bv):
     assert err.max() <= TOL
 
 
+@pytest.mark.parametrize("bk,bv", [(2, 2), (4, 2)])
+def test_decode_ragged_lengths_across_splits(dev, bk, bv):
+    """Several tiles per split (8 sequences x 4 KV heads, 100-tile capacity: 25
+    splits of 4 tiles) with lengths that end inside a split, on a split
+    boundary, after one tile, at zero and at the capacity."""
+    batch, hkv, gs, max_tiles = 8, 4, 4, 100
+    hq = gs * hkv
+    kr, vr = _cache(batch * hkv * max_tiles, bk, bv, seed=77 + bk)
+    q = np.random.default_rng(78).standard_normal((batch, hq, 128)).astype(np.float16)
+    n_tiles = np.array([100, 0, 1, 37, 64, 99, 3, 52], np.int32)
+    got = _run(dev, q, kr, vr, n_tiles, hkv, max_tiles, bk, bv)
+    ref = oracle.decode_attn(q.view(np.uint16), kr, vr, n_tiles, hq, hkv, max_tiles, bk, bv)
+    empty = n_tiles == 0
+    assert np.all(got[empty] == 0.0)          # no tokens: zero output
+    err = parity.rel_l2_rows(got[~empty], ref[~empty])
+    _log(bk, bv, "max rel l2", err.max())
+    assert err.max() <= TOL
+
+
 @pytest.mark.parametrize("sm_scale", [0.0, 2.0 ** -20, 0.5, -0.088, 3.0])
 def test_decode_softmax_scales(dev, sm_scale):
     """Softmax scales from zero (uniform weights) to sharp, and negative."""
