@@ -188,7 +188,9 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
  *   n_records       number of records in k_packed and in v_packed; table
  *                   entries outside [0, n_records) contribute nothing
  *   n_q_heads       multiple of n_kv_heads, at most 8 query heads per KV head;
- *                   batch and n_kv_heads at most 65535
+ *                   batch at most 65535, and n_kv_heads times the number of
+ *                   4-query chunks per KV head (1 or 2) at most 65535
+ *                   (KVARN_EUNSUPPORTED otherwise)
  *   bits_k, bits_v  2 or 4
  *   sm_scale        softmax scale, 1/sqrt(128) for standard attention; zero or
  *                   2^-32 <= |sm_scale| <= 2^32 (KVARN_EINVAL otherwise)

@@ -138,7 +138,8 @@ int kvarn_decode_attn_windows(const void* q, const void* k_packed, const void* v
                        recent_cap > 65536))
         return KVARN_EINVAL;
     if (!valid_bits(bits_k) || !valid_bits(bits_v) || n_q_heads / n_kv_heads > 8) return KVARN_EUNSUPPORTED;
-    if (batch > 65535 || n_kv_heads > 65535) return KVARN_EUNSUPPORTED;  // grid y/z limits
+    // grid limits: z = batch, y = n_kv_heads x chunks of 4 query heads
+    if (batch > 65535 || (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 3) / 4) > 65535) return KVARN_EUNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_packed) || !aligned16(v_packed) || !aligned16(out)) return KVARN_EALIGN;
     if ((reinterpret_cast<uintptr_t>(n_tiles_per_seq) & 3u) != 0 ||
         (block_table != nullptr && (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))

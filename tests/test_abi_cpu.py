@@ -110,6 +110,8 @@ def test_decode_argument_errors():
     assert da(hq=6, hkv=4) == kvarn.EINVAL
     assert da(hq=32, hkv=2) == kvarn.EUNSUPPORTED  # 16 query heads per KV head
     assert da(bk=3) == kvarn.EUNSUPPORTED
+    assert da(b=65536) == kvarn.EUNSUPPORTED                 # grid z
+    assert da(hq=8 * 40000, hkv=40000) == kvarn.EUNSUPPORTED  # grid y: 40000 KV heads x 2 chunks
     assert da(qp=MIS) == kvarn.EALIGN
     assert da(ws=None) == kvarn.EWORKSPACE
     assert da(wsb=16) == kvarn.EWORKSPACE
