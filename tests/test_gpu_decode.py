@@ -268,3 +268,73 @@ def test_decode_windows_only(dev):
     err = parity.rel_l2_rows(out.float().cpu().numpy(), ref)
     _log("windows only max rel l2", err.max())
     assert err.max() <= TOL
+
+
+def test_streaming_cache_block_fill(dev):
+    """The streaming cache around the kernels: an FP16 sink (128 tokens), the
+    packed body and an FP16 trailing window of capacity 128.  Tokens are appended
+    one by one; when a sequence's trailing window fills, the block is quantised
+    straight out of the window buffer (tile offsets into it) into the next free
+    records of a shared pool (destination indices), the block table gains the
+    record and the window restarts.  Decode attention over the three regions is
+    checked against the oracle after each fill and at the end, with the
+    sequences at different lengths."""
+    batch, hkv, gs, n_sink, cap, max_tiles = 2, 2, 4, 128, 128, 4
+    hq = gs * hkv
+    rng = np.random.default_rng(91)
+    lengths = [n_sink + 3 * cap + 50, n_sink + 2 * cap + 127]            # tokens per sequence
+    T = max(lengths)
+    kx = (rng.standard_normal((batch, hkv, T, 128)) * np.exp(rng.normal(0, 0.5, (1, hkv, 1, 128)))).astype(np.float16)
+    vx = rng.standard_normal((batch, hkv, T, 128)).astype(np.float16)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    u16 = lambda a: np.ascontiguousarray(a).view(np.uint16)  # noqa: E731
+    pb = kvarn.tile_bytes(2)
+    pool_k = torch.zeros((batch * hkv * max_tiles, pb), dtype=torch.uint8, device=dev)
+    pool_v = torch.zeros_like(pool_k)
+    table = torch.full((batch * hkv * max_tiles,), -1, dtype=torch.int32, device=dev)
+    n_tiles = torch.zeros(batch, dtype=torch.int32, device=dev)
+    sink_k, sink_v = d(kx[:, :, :n_sink]), d(vx[:, :, :n_sink])
+    rec_k = torch.zeros((batch, hkv, cap, 128), dtype=torch.float16, device=dev)
+    rec_v = torch.zeros_like(rec_k)
+    n_recent = torch.zeros(batch, dtype=torch.int32, device=dev)
+    next_record = 0
+    q = rng.standard_normal((batch, hq, 128)).astype(np.float16)
+    checks = 0
+
+    def check(tag):
+        out = kvarn.decode_attn(d(q), pool_k, pool_v, n_tiles, hkv, max_tiles, 2, 2, block_table=table,
+                                k_sink=sink_k, v_sink=sink_v, k_recent=rec_k, v_recent=rec_v, n_recent=n_recent)
+        torch.cuda.synchronize()
+        ref = oracle.decode_attn(u16(q), pool_k.cpu().numpy(), pool_v.cpu().numpy(), n_tiles.cpu().numpy(), hq, hkv,
+                                 max_tiles, 2, 2, block_table=table.cpu().numpy(),
+                                 k_sink=u16(sink_k.cpu().numpy()), v_sink=u16(sink_v.cpu().numpy()),
+                                 k_recent=u16(rec_k.cpu().numpy()), v_recent=u16(rec_v.cpu().numpy()),
+                                 n_recent=n_recent.cpu().numpy())
+        err = parity.rel_l2_rows(out.float().cpu().numpy(), ref)
+        _log("streaming", tag, "tiles", n_tiles.tolist(), "recent", n_recent.tolist(), "max rel l2", err.max())
+        assert err.max() <= TOL
+
+    for t in range(n_sink, T):
+        for b in range(batch):
+            if t >= lengths[b]:
+                continue
+            r = int(n_recent[b])
+            rec_k[b, :, r] = d(kx[b, :, t])
+            rec_v[b, :, r] = d(vx[b, :, t])
+            n_recent[b] = r + 1
+            if r + 1 == cap:                                   # block full: into the body
+                j = int(n_tiles[b])
+                offs = torch.tensor([(b * hkv + h) * cap * 128 for h in range(hkv)], dtype=torch.int64, device=dev)
+                dst = torch.arange(next_record, next_record + hkv, dtype=torch.int64, device=dev)
+                kvarn.quantize_tiles(rec_k, hkv, 2, K, tile_offset=offs, out=pool_k, dst_index=dst)
+                kvarn.quantize_tiles(rec_v, hkv, 2, V, tile_offset=offs, out=pool_v, dst_index=dst)
+                for h in range(hkv):
+                    table[(b * hkv + h) * max_tiles + j] = next_record + h
+                next_record += hkv
+                n_tiles[b] = j + 1
+                n_recent[b] = 0
+                checks += 1
+                check(f"after fill {checks}")
+    check("end")
+    # the pool holds exactly the quantised blocks, in fill order
+    assert next_record == sum((L - n_sink) // cap for L in lengths) * hkv
