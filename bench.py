@@ -101,6 +101,9 @@ class OpTimer:
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
 
 
+EVENT_EVERY = 10   # codec steps per step timed launch by launch
+
+
 def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2, with_variants=True):
     dev = torch.device("cuda:0")
     log(f"generating decode-append inputs {layers}x{seqs}x128x{heads}x128 bf16")
@@ -136,9 +139,12 @@ def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2, with_variant
         step(False)
     torch.cuda.synchronize()
     log(f"timing {steps} steps")
+    # Every tenth step carries HIP events around each launch: each recorded
+    # event costs the stream a few microseconds, so events on every launch
+    # would add ~4 % to the step they are meant to describe.
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step(True)
+    for i in range(steps):
+        step(i % EVENT_EVERY == 0)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_op = {name: t.mean_ms() for name, t in timers.items()}
