@@ -88,8 +88,17 @@ def workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_tiles: int)
 _DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 
 
-def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+def _ptr(t, dtype=None):
+    """Device address of tensor t (None passes NULL).  The kernels dereference it
+    on the GPU, so a host tensor is refused here; index tensors must also have
+    the element type the C ABI reads."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libkvarn takes device tensors; got one on " + str(t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"expected a {dtype} tensor, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
@@ -110,8 +119,9 @@ def quantize_tiles(x: torch.Tensor, n_tiles: int, bits: int, axis: int, *, tile_
     """Quantise tiles of ``x`` (fp16/bf16/fp32 on the GPU) into packed uint8 records [n, Pb]."""
     if out is None:
         out = torch.empty((n_tiles, tile_bytes(bits)), dtype=torch.uint8, device=x.device)
-    st = load().kvarn_quantize_tiles(_ptr(x), _DT[x.dtype], n_tiles, tile_stride, token_stride, _ptr(tile_offset),
-                                     bits, axis, n_iter, _ptr(out), _ptr(dst_index), flags, _stream(stream))
+    st = load().kvarn_quantize_tiles(_ptr(x), _DT[x.dtype], n_tiles, tile_stride, token_stride,
+                                     _ptr(tile_offset, torch.int64), bits, axis, n_iter, _ptr(out),
+                                     _ptr(dst_index, torch.int64), flags, _stream(stream))
     _check("kvarn_quantize_tiles", st)
     return out
 
@@ -126,8 +136,9 @@ def dequantize_tiles(packed: torch.Tensor, n_tiles: int, bits: int, axis: int, o
                      tile_stride: int = TILE * HEAD_DIM, token_stride: int = HEAD_DIM,
                      src_index: torch.Tensor | None = None, dst_offset: torch.Tensor | None = None,
                      flags: int = 0, stream=None) -> torch.Tensor:
-    st = load().kvarn_dequantize_tiles(_ptr(packed), _ptr(src_index), n_tiles, bits, axis, _ptr(out),
-                                       _DT[out.dtype], tile_stride, token_stride, _ptr(dst_offset), flags,
+    st = load().kvarn_dequantize_tiles(_ptr(packed), _ptr(src_index, torch.int64), n_tiles, bits, axis,
+                                       _ptr(out), _DT[out.dtype], tile_stride, token_stride,
+                                       _ptr(dst_offset, torch.int64), flags,
                                        _stream(stream))
     _check("kvarn_dequantize_tiles", st)
     return out
@@ -163,18 +174,19 @@ def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     n_records = min(k_packed.shape[0], v_packed.shape[0])
     if k_sink is None and k_recent is None:
-        st = load().kvarn_decode_attn(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table),
-                                      _ptr(n_tiles_per_seq), n_records, batch, n_q_heads, n_kv_heads, max_tiles,
-                                      bits_k, bits_v, float(sm_scale), _ptr(out), _ptr(workspace),
+        st = load().kvarn_decode_attn(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table, torch.int32),
+                                      _ptr(n_tiles_per_seq, torch.int32), n_records, batch, n_q_heads, n_kv_heads,
+                                      max_tiles, bits_k, bits_v, float(sm_scale), _ptr(out), _ptr(workspace),
                                       workspace.numel(), flags, _stream(stream))
         _check("kvarn_decode_attn", st)
         return out
     n_sink = 0 if k_sink is None else k_sink.shape[2]
     cap = 0 if k_recent is None else k_recent.shape[2]
-    st = load().kvarn_decode_attn_windows(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table),
-                                          _ptr(n_tiles_per_seq), n_records, batch, n_q_heads, n_kv_heads, max_tiles,
-                                          bits_k, bits_v, float(sm_scale), _ptr(k_sink), _ptr(v_sink), n_sink,
-                                          _ptr(k_recent), _ptr(v_recent), _ptr(n_recent), cap, _ptr(out),
+    st = load().kvarn_decode_attn_windows(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table, torch.int32),
+                                          _ptr(n_tiles_per_seq, torch.int32), n_records, batch, n_q_heads,
+                                          n_kv_heads, max_tiles, bits_k, bits_v, float(sm_scale), _ptr(k_sink),
+                                          _ptr(v_sink), n_sink,
+                                          _ptr(k_recent), _ptr(v_recent), _ptr(n_recent, torch.int32), cap, _ptr(out),
                                           _ptr(workspace), workspace.numel(), flags, _stream(stream))
     _check("kvarn_decode_attn_windows", st)
     return out

@@ -129,3 +129,14 @@ def test_decode_workspace_plan():
     assert kvarn.workspace_bytes(16, 32, 8, 256) == 16 * 32 * 8 * 136 * 4
     assert kvarn.workspace_bytes(1, 4, 1, 3) == 1 * 4 * 3 * 136 * 4
     assert kvarn.workspace_bytes(2, 4, 1, 0) == 2 * 4 * 1 * 136 * 4
+
+
+def test_binding_refuses_host_tensors_and_wrong_index_types():
+    """The kernels dereference every pointer on the GPU: the binding refuses a
+    host tensor, and index tensors of the wrong element type, before calling in."""
+    import torch
+    x = torch.zeros((1, 128, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        kvarn.quantize_tiles(x, 1, 2, kvarn.AXIS_K)
+    with pytest.raises(ValueError):
+        kvarn.dequantize_tiles(torch.zeros((1, kvarn.tile_bytes(2)), dtype=torch.uint8), 1, 2, kvarn.AXIS_K, x)
