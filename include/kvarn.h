@@ -62,6 +62,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* hipStream_t.  A C or C++ client built with gcc or another compiler than hipcc
+ * defines __HIP_PLATFORM_AMD__ (hipcc does so itself) and adds /opt/rocm/include
+ * to its include path. */
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus

@@ -3,6 +3,8 @@ declared in include/kvarn.h, and rejects bad arguments before any HIP call."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -125,7 +127,7 @@ def test_decode_argument_errors():
 
 
 def test_decode_workspace_plan():
-    # 16 sequences x 8 KV heads x 256 tiles -> 16 splits of 16 tiles
+    # 16 sequences x 8 KV heads x 256 tiles -> 8 splits of 32 tiles (1024 waves)
     assert kvarn.workspace_bytes(16, 32, 8, 256) == 16 * 32 * 8 * 136 * 4
     assert kvarn.workspace_bytes(1, 4, 1, 3) == 1 * 4 * 3 * 136 * 4
     assert kvarn.workspace_bytes(2, 4, 1, 0) == 2 * 4 * 1 * 136 * 4
@@ -140,3 +142,19 @@ def test_binding_refuses_host_tensors_and_wrong_index_types():
         kvarn.quantize_tiles(x, 1, 2, kvarn.AXIS_K)
     with pytest.raises(ValueError):
         kvarn.dequantize_tiles(torch.zeros((1, kvarn.tile_bytes(2)), dtype=torch.uint8), 1, 2, kvarn.AXIS_K, x)
+
+
+def test_plain_c_client_builds_links_and_runs(tmp_path):
+    """include/kvarn.h compiles as C11 and the library links and runs from C
+    without Python (tests/c_client/abi_client.c; no call reaches the GPU)."""
+    gcc, rocm_inc = shutil.which("gcc"), "/opt/rocm/include"
+    if gcc is None or not os.path.isdir(rocm_inc):
+        pytest.skip("needs gcc and the ROCm headers")
+    libdir = os.path.dirname(kvarn.LIB_PATH)
+    exe = str(tmp_path / "abi_client")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", rocm_inc,
+                    os.path.join(ROOT, "tests", "c_client", "abi_client.c"),
+                    "-L", libdir, "-lkvarn", "-Wl,-rpath," + libdir, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
