@@ -130,7 +130,8 @@ const char *kvarn_status_string(int status);
  * Experiments, Efficiency); n_iter = 0 skips the normalisation.
  *
  *   x               device, element type x_dtype (KVARN_F16 / BF16 / F32)
- *   n_tiles         >= 0; 0 is a no-op
+ *   n_tiles         >= 0; 0 is a no-op.  A batch of more than 2^23 tiles runs
+ *                   as consecutive launches of 2^23 tiles on the stream.
  *   tile_stride     elements between consecutive tiles when tile_offset is NULL
  *   token_stride    elements between consecutive tokens of a tile (>= 128)
  *   tile_offset     device int64[n_tiles] element offsets of the tiles, or NULL
@@ -164,7 +165,7 @@ int kvarn_quantize_tiles(const void *x, int x_dtype, int64_t n_tiles, int64_t ti
  *   out_dtype       KVARN_F16, KVARN_BF16 (round to nearest even) or KVARN_F32
  *   flags           the flags the records were written with
  *
- * Alignment as for kvarn_quantize_tiles (out in place of x).
+ * n_tiles and alignment as for kvarn_quantize_tiles (out in place of x).
  */
 int kvarn_dequantize_tiles(const void *packed, const int64_t *src_tile_index, int64_t n_tiles, int bits, int axis,
                            void *out, int out_dtype, int64_t tile_stride, int64_t token_stride,

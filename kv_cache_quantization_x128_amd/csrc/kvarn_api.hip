@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "kvarn.h"
 #include "kvarn_launch.h"
 
@@ -14,7 +16,12 @@ using kvarn::QuantizeArgs;
 
 namespace {
 
-constexpr int64_t kMaxTilesPerLaunch = 0x7FFFFFFF;  // grid x limit
+// One workgroup of 256 threads per tile, and a launch covers fewer than 2^32
+// threads: larger batches are cut into launches of 2^23 tiles, in order, on the
+// caller's stream.
+constexpr int64_t kTilesPerLaunch = int64_t(1) << 23;
+
+int64_t elem_bytes(int dtype) { return dtype == KVARN_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_bits(int b) { return b == 2 || b == 4; }
@@ -32,7 +39,6 @@ int hip_status(hipError_t e) {
 int check_tiles(const void* buf, int64_t n_tiles, int64_t tile_stride, int64_t token_stride, const int64_t* offs) {
     if (buf == nullptr || n_tiles < 0 || token_stride < KVARN_HEAD_DIM) return KVARN_EINVAL;
     if (offs == nullptr && tile_stride < 0) return KVARN_EINVAL;
-    if (n_tiles > kMaxTilesPerLaunch) return KVARN_EINVAL;
     if (!aligned16(buf)) return KVARN_EALIGN;
     if ((token_stride & 7) != 0 || (offs == nullptr && (tile_stride & 7) != 0)) return KVARN_EALIGN;
     if (offs != nullptr && (reinterpret_cast<uintptr_t>(offs) & 7u) != 0) return KVARN_EALIGN;
@@ -82,9 +88,18 @@ int kvarn_quantize_tiles(const void* x, int x_dtype, int64_t n_tiles, int64_t ti
     if (!aligned16(packed)) return KVARN_EALIGN;
     if (dst_tile_index != nullptr && (reinterpret_cast<uintptr_t>(dst_tile_index) & 7u) != 0) return KVARN_EALIGN;
     if (n_tiles == 0) return KVARN_OK;
-    QuantizeArgs a{x, x_dtype, n_tiles, tile_stride, token_stride, tile_offset, bits, axis, n_iter,
-                   static_cast<uint8_t*>(packed), dst_tile_index, (flags & KVARN_NO_ROTATION) ? 0 : 1, stream};
-    return hip_status(kvarn::launch_quantize(a));
+    for (int64_t base = 0; base < n_tiles; base += kTilesPerLaunch) {
+        // tiles base.. of the batch: their offsets and record indices, or the
+        // identity layouts advanced by base tiles
+        const void* xb = tile_offset ? x : static_cast<const char*>(x) + base * tile_stride * elem_bytes(x_dtype);
+        uint8_t* pb = static_cast<uint8_t*>(packed) + (dst_tile_index ? 0 : base * (int64_t)kvarn_tile_bytes(bits));
+        QuantizeArgs a{xb, x_dtype, std::min(kTilesPerLaunch, n_tiles - base), tile_stride, token_stride,
+                       tile_offset ? tile_offset + base : nullptr, bits, axis, n_iter, pb,
+                       dst_tile_index ? dst_tile_index + base : nullptr, (flags & KVARN_NO_ROTATION) ? 0 : 1, stream};
+        const int r = hip_status(kvarn::launch_quantize(a));
+        if (r != KVARN_OK) return r;
+    }
+    return KVARN_OK;
 }
 
 int kvarn_dequantize_tiles(const void* packed, const int64_t* src_tile_index, int64_t n_tiles, int bits, int axis,
@@ -97,9 +112,18 @@ int kvarn_dequantize_tiles(const void* packed, const int64_t* src_tile_index, in
     if (!aligned16(packed)) return KVARN_EALIGN;
     if (src_tile_index != nullptr && (reinterpret_cast<uintptr_t>(src_tile_index) & 7u) != 0) return KVARN_EALIGN;
     if (n_tiles == 0) return KVARN_OK;
-    DequantizeArgs a{static_cast<const uint8_t*>(packed), src_tile_index, n_tiles, bits, axis, out, out_dtype,
-                     tile_stride, token_stride, dst_tile_offset, (flags & KVARN_NO_ROTATION) ? 0 : 1, stream};
-    return hip_status(kvarn::launch_dequantize(a));
+    for (int64_t base = 0; base < n_tiles; base += kTilesPerLaunch) {
+        const uint8_t* pb =
+            static_cast<const uint8_t*>(packed) + (src_tile_index ? 0 : base * (int64_t)kvarn_tile_bytes(bits));
+        void* ob = dst_tile_offset ? out : static_cast<char*>(out) + base * tile_stride * elem_bytes(out_dtype);
+        DequantizeArgs a{pb, src_tile_index ? src_tile_index + base : nullptr, std::min(kTilesPerLaunch, n_tiles - base),
+                         bits, axis, ob, out_dtype, tile_stride, token_stride,
+                         dst_tile_offset ? dst_tile_offset + base : nullptr, (flags & KVARN_NO_ROTATION) ? 0 : 1,
+                         stream};
+        const int r = hip_status(kvarn::launch_dequantize(a));
+        if (r != KVARN_OK) return r;
+    }
+    return KVARN_OK;
 }
 
 // The softmax scale rides on the query's power-of-two block scale, which must

@@ -225,6 +225,42 @@ def test_empty_batch_is_noop(dev):
     assert (out == 7).all()
 
 
+def test_batch_larger_than_one_launch(dev):
+    """A call with more than 2^23 tiles runs as several launches of at most 2^23
+    tiles; tiles of the second launch are quantised and dequantised exactly like
+    those of the first.  Every tile reads the same input tile (all offsets 0) and
+    writes its own record (38.7 GB of records).  Dequantisation reads record 0
+    for every tile; the first 2^23 output tiles go to slots i % 4096 (every
+    writer of a slot stores the same bytes) and the last 5 to slots 4096..4100.
+    The single record is checked against the oracle."""
+    n_first, n_tail, ring = 1 << 23, 5, 4096
+    n = n_first + n_tail
+    k, _ = synth.tiny()
+    tile = np.ascontiguousarray(k[0, 0, :128])
+    x = torch.from_numpy(tile).reshape(1, 128, 128).to(dev)
+    ref = _gpu_quantize_dense(x, 2, K)
+    view = oracle.TileView.dense(tiles_bits(tile.reshape(1, 128, 128)), oracle.DT_F16)
+    parity.assert_quantize_parity(parity.compare_quantize(view, 2, K, ref))
+
+    _log("quantise", n, "tiles in one call")
+    rec = torch.zeros((n, kvarn.tile_bytes(2)), dtype=torch.uint8, device=dev)
+    kvarn.quantize_tiles(x, n, 2, K, tile_offset=torch.zeros(n, dtype=torch.int64, device=dev), out=rec)
+    ref_dev = torch.from_numpy(ref).to(dev)
+    for r0 in range(0, n, 1 << 20):
+        assert bool((rec[r0:r0 + (1 << 20)] == ref_dev).all()), r0
+    del rec
+
+    one = kvarn.dequantize(ref_dev, 2, K, torch.float16)
+    slot = torch.arange(n, dtype=torch.int64, device=dev) % ring
+    slot[n_first:] = ring + torch.arange(n_tail, dtype=torch.int64, device=dev)
+    _log("dequantise", n, "tiles in one call")
+    out = torch.full((ring + n_tail, 128, 128), float("nan"), dtype=torch.float16, device=dev)
+    kvarn.dequantize_tiles(ref_dev, n, 2, K, out, src_index=torch.zeros(n, dtype=torch.int64, device=dev),
+                           dst_offset=slot * (128 * 128))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), one.expand_as(out).view(torch.int16))
+
+
 # ------------------------------------------------------------------------------------- full sizes
 def _sample_dense(x_flat, offsets, idx, token_stride):
     """Gather tiles (exact bytes) at offsets[idx] of a flat 16-bit tensor into [n,128,128]."""
