@@ -63,17 +63,20 @@ class StreamingKVCache:
         rest starts the trailing window."""
         if self._prefilled:
             raise RuntimeError("prefill() is called once, before append()")
+        self._check_tokens(k, v, 4)
         T = k.shape[2]
         lengths = [T] * self.batch if lengths is None else [int(x) for x in lengths]
+        if len(lengths) != self.batch:
+            raise ValueError("one length per sequence")
         if any(L < self.n_sink or L > T for L in lengths):
-            raise ValueError("every sequence needs at least the sink's tokens")
+            raise ValueError("every sequence needs at least the sink's tokens, and at most T")
+        if any((L - self.n_sink) // TILE > self.max_tiles for L in lengths):
+            raise ValueError("prompt longer than the cache's capacity")
         if self.n_sink:
             self.sink_k.copy_(k[:, :, :self.n_sink])
             self.sink_v.copy_(v[:, :, :self.n_sink])
         for b, L in enumerate(lengths):
             n_blocks = (L - self.n_sink) // TILE
-            if self._tiles[b] + n_blocks > self.max_tiles:
-                raise ValueError("prompt longer than the cache's capacity")
             for j in range(n_blocks):
                 t0 = self.n_sink + j * TILE
                 self.recent_k[b].copy_(k[b, :, t0:t0 + TILE])
@@ -94,25 +97,38 @@ class StreamingKVCache:
         trailing window fills get that block quantised into the body."""
         if not self._prefilled:
             raise RuntimeError("prefill() first (the sink needs its tokens)")
+        self._check_tokens(k, v, 3)
         seqs = list(range(self.batch)) if active is None else [int(b) for b in active]
+        if len(set(seqs)) != len(seqs) or any(b < 0 or b >= self.batch for b in seqs):
+            raise ValueError("active sequences must be distinct indices below batch")
         if not seqs:
             return
+        # every check before the first write: a refused call leaves the cache as it was
+        full = [b for b in seqs if self._recent[b] + 1 == self.cap]
+        if any(self._tiles[b] >= self.max_tiles for b in full):
+            raise RuntimeError("a sequence outgrew the cache's capacity")
         idx = torch.tensor(seqs, device=k.device, dtype=torch.int64)
         pos = torch.tensor([self._recent[b] for b in seqs], device=k.device, dtype=torch.int64)
         self.recent_k[idx, :, pos] = k[idx]
         self.recent_v[idx, :, pos] = v[idx]
-        full = []
         for b in seqs:
             self._recent[b] += 1
-            if self._recent[b] == self.cap:
-                full.append(b)
         if full:
-            if any(self._tiles[b] >= self.max_tiles for b in full):
-                raise RuntimeError("a sequence outgrew the cache's capacity")
             self._commit(full)
             for b in full:
                 self._recent[b] = 0
         self.n_recent.copy_(torch.tensor(self._recent, dtype=torch.int32))
+
+    def _check_tokens(self, k: torch.Tensor, v: torch.Tensor, ndim: int) -> None:
+        """k and v: fp16 on the cache's device, [batch][n_kv_heads][T][128] (ndim 4,
+        prefill) or [batch][n_kv_heads][128] (ndim 3, append)."""
+        for t in (k, v):
+            if (t.dtype != torch.float16 or t.device != self.recent_k.device or t.dim() != ndim or
+                    t.shape[:2] != (self.batch, self.n_kv_heads) or t.shape[-1] != 128):
+                raise ValueError(f"expected fp16 [{self.batch}][{self.n_kv_heads}]{'[T]' if ndim == 4 else ''}[128] "
+                                 f"on {self.recent_k.device}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+        if k.shape != v.shape:
+            raise ValueError("k and v differ in shape")
 
     def _commit(self, seqs) -> None:
         """Quantise the full trailing windows of `seqs` (all their KV heads) into

@@ -79,5 +79,7 @@ def test_stream_cache_rejects_misuse(dev):
         c.prefill(x, x)                               # fewer tokens than the sink
     y = torch.zeros((1, 1, 128 + 128 + 127, 128), dtype=torch.float16, device=dev)
     c.prefill(y, y)
-    with pytest.raises(RuntimeError):
-        c.append(y[:, :, 0], y[:, :, 0])             # the window fills but the body is full
+    for _ in range(2):                                # refused calls leave the cache as it was
+        with pytest.raises(RuntimeError):
+            c.append(y[:, :, 0], y[:, :, 0])         # the window fills but the body is full
+        assert c.tokens(0) == 128 + 128 + 127 and c.n_recent.tolist() == [127]
