@@ -101,6 +101,44 @@ def _ptr(t, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+# Size checks on tensor metadata only (no device reads, no synchronisation): the
+# kernels read and write the memory the arguments describe, so a tensor that is
+# smaller than that, or not contiguous, is refused before the call instead of
+# being read or written out of bounds on the GPU.  Index and offset values are
+# the caller's to keep inside the buffers (the header says so).
+def _nbytes(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.numel() * t.element_size()
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_index(t, n, name, dtype):
+    if t is not None:
+        _need(t.dtype == dtype, f"{name}: expected {dtype}, got {t.dtype}")
+        _need(_nbytes(t, name) >= n * t.element_size(), f"{name} has fewer than {n} entries")
+
+
+def _check_tiles(buf, n_tiles, tile_stride, token_stride, offsets, name):
+    """buf covers n_tiles tiles at these strides (or offsets has n_tiles entries)."""
+    _check_index(offsets, n_tiles, name + " offsets", torch.int64)
+    if offsets is None and n_tiles > 0 and tile_stride >= 0 and token_stride >= HEAD_DIM:
+        last = (n_tiles - 1) * tile_stride + (TILE - 1) * token_stride + HEAD_DIM
+        _need(_nbytes(buf, name) >= last * buf.element_size(),
+              f"{name} holds fewer than {n_tiles} tiles at tile_stride {tile_stride}, token_stride {token_stride}")
+
+
+def _check_records(buf, n_tiles, bits, index, name):
+    """buf holds n_tiles records (or index has n_tiles entries)."""
+    _check_index(index, n_tiles, name + " index", torch.int64)
+    if index is None and n_tiles > 0:
+        _need(_nbytes(buf, name) >= n_tiles * tile_bytes(bits), f"{name} holds fewer than {n_tiles} records")
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -119,6 +157,8 @@ def quantize_tiles(x: torch.Tensor, n_tiles: int, bits: int, axis: int, *, tile_
     """Quantise tiles of ``x`` (fp16/bf16/fp32 on the GPU) into packed uint8 records [n, Pb]."""
     if out is None:
         out = torch.empty((n_tiles, tile_bytes(bits)), dtype=torch.uint8, device=x.device)
+    _check_tiles(x, n_tiles, tile_stride, token_stride, tile_offset, "x")
+    _check_records(out, n_tiles, bits, dst_index, "out")
     st = load().kvarn_quantize_tiles(_ptr(x), _DT[x.dtype], n_tiles, tile_stride, token_stride,
                                      _ptr(tile_offset, torch.int64), bits, axis, n_iter, _ptr(out),
                                      _ptr(dst_index, torch.int64), flags, _stream(stream))
@@ -136,6 +176,8 @@ def dequantize_tiles(packed: torch.Tensor, n_tiles: int, bits: int, axis: int, o
                      tile_stride: int = TILE * HEAD_DIM, token_stride: int = HEAD_DIM,
                      src_index: torch.Tensor | None = None, dst_offset: torch.Tensor | None = None,
                      flags: int = 0, stream=None) -> torch.Tensor:
+    _check_records(packed, n_tiles, bits, src_index, "packed")
+    _check_tiles(out, n_tiles, tile_stride, token_stride, dst_offset, "out")
     st = load().kvarn_dequantize_tiles(_ptr(packed), _ptr(src_index, torch.int64), n_tiles, bits, axis,
                                        _ptr(out), _DT[out.dtype], tile_stride, token_stride,
                                        _ptr(dst_offset, torch.int64), flags,
@@ -164,20 +206,38 @@ def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
     Optional FP16 windows around the packed body: k_sink / v_sink
     [batch][n_kv_heads][n_sink][128]; k_recent / v_recent
     [batch][n_kv_heads][recent_cap][128] with n_recent int32 [batch] valid tokens."""
+    _need(q.dim() == 3 and q.shape[2] == HEAD_DIM and q.dtype == torch.float16, "q: fp16 [batch][n_q_heads][128]")
     batch, n_q_heads, _ = q.shape
+    _nbytes(q, "q")
     if sm_scale is None:
         sm_scale = HEAD_DIM ** -0.5
     if out is None:
         out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == torch.float16 and out.is_contiguous(), "out: contiguous, like q")
     need = workspace_bytes(batch, n_q_heads, n_kv_heads, max_tiles)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    n_records = min(k_packed.shape[0], v_packed.shape[0])
+    ws_bytes = _nbytes(workspace, "workspace")
+    _check_index(n_tiles_per_seq, batch, "n_tiles_per_seq", torch.int32)
+    _check_index(block_table, batch * n_kv_heads * max(max_tiles, 0), "block_table", torch.int32)
+    # records past the end of either buffer count as missing tiles in the kernel
+    tbk, tbv = tile_bytes(bits_k), tile_bytes(bits_v)
+    n_records = min(_nbytes(k_packed, "k_packed") // tbk, _nbytes(v_packed, "v_packed") // tbv) if tbk and tbv else 0
+    for kw, vw, name in ((k_sink, v_sink, "sink"), (k_recent, v_recent, "recent")):
+        if kw is not None or vw is not None:
+            _need(kw is not None and vw is not None and kw.shape == vw.shape, f"k_{name} and v_{name} go together")
+            _need(kw.dim() == 4 and tuple(kw.shape[:2]) == (batch, n_kv_heads) and kw.shape[3] == HEAD_DIM and
+                  kw.dtype == torch.float16 and vw.dtype == torch.float16,
+                  f"{name} windows: fp16 [batch][n_kv_heads][n][128]")
+            _nbytes(kw, "k_" + name), _nbytes(vw, "v_" + name)
+    if k_recent is not None:
+        _need(n_recent is not None, "n_recent goes with the recent windows")
+        _check_index(n_recent, batch, "n_recent", torch.int32)
     if k_sink is None and k_recent is None:
         st = load().kvarn_decode_attn(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table, torch.int32),
                                       _ptr(n_tiles_per_seq, torch.int32), n_records, batch, n_q_heads, n_kv_heads,
                                       max_tiles, bits_k, bits_v, float(sm_scale), _ptr(out), _ptr(workspace),
-                                      workspace.numel(), flags, _stream(stream))
+                                      ws_bytes, flags, _stream(stream))
         _check("kvarn_decode_attn", st)
         return out
     n_sink = 0 if k_sink is None else k_sink.shape[2]
@@ -187,6 +247,6 @@ def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
                                           n_kv_heads, max_tiles, bits_k, bits_v, float(sm_scale), _ptr(k_sink),
                                           _ptr(v_sink), n_sink,
                                           _ptr(k_recent), _ptr(v_recent), _ptr(n_recent, torch.int32), cap, _ptr(out),
-                                          _ptr(workspace), workspace.numel(), flags, _stream(stream))
+                                          _ptr(workspace), ws_bytes, flags, _stream(stream))
     _check("kvarn_decode_attn_windows", st)
     return out

@@ -158,3 +158,50 @@ def test_plain_c_client_builds_links_and_runs(tmp_path):
                     "-L", libdir, "-lkvarn", "-Wl,-rpath," + libdir, "-o", exe], check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+
+
+def test_binding_checks_sizes_before_calling():
+    """Tensors smaller than what a call reads or writes, or not contiguous, are
+    refused from their metadata alone (these CPU tensors never reach the library:
+    the size checks come first, the device check after them)."""
+    import torch
+    f16, i64, i32, u8 = torch.float16, torch.int64, torch.int32, torch.uint8
+    x = torch.zeros((2, 128, 128), dtype=f16)
+    rec = torch.zeros((2, kvarn.tile_bytes(2)), dtype=u8)
+    cases = [
+        lambda: kvarn.quantize_tiles(x, 3, 2, kvarn.AXIS_K, out=rec),                         # x holds 2 tiles
+        lambda: kvarn.quantize_tiles(x, 2, 2, kvarn.AXIS_K, token_stride=256, out=rec),       # strided past the end
+        lambda: kvarn.quantize_tiles(x, 2, 2, kvarn.AXIS_K, out=rec[:1]),                     # room for 1 record
+        lambda: kvarn.quantize_tiles(x, 2, 2, kvarn.AXIS_K, out=rec, tile_offset=torch.zeros(1, dtype=i64)),
+        lambda: kvarn.quantize_tiles(x, 2, 2, kvarn.AXIS_K, out=rec, dst_index=torch.zeros(2, dtype=i32)),
+        lambda: kvarn.quantize_tiles(x.transpose(1, 2), 2, 2, kvarn.AXIS_K, out=rec),        # not contiguous
+        lambda: kvarn.dequantize_tiles(rec, 3, 2, kvarn.AXIS_K, torch.zeros((3, 128, 128), dtype=f16)),
+        lambda: kvarn.dequantize_tiles(rec, 2, 2, kvarn.AXIS_K, x[:1]),
+        lambda: kvarn.dequantize_tiles(rec, 2, 4, kvarn.AXIS_K, x),                           # 4-bit records are larger
+    ]
+    q = torch.zeros((2, 8, 128), dtype=f16)
+    nt = torch.zeros(2, dtype=i32)
+    kp = torch.zeros((16, kvarn.tile_bytes(2)), dtype=u8)
+    cases += [
+        lambda: kvarn.decode_attn(q.float(), kp, kp, nt, 2, 4, 2, 2),                         # q not fp16
+        lambda: kvarn.decode_attn(q[:, :, :64], kp, kp, nt, 2, 4, 2, 2),                      # head_dim 64
+        lambda: kvarn.decode_attn(q, kp, kp, nt[:1], 2, 4, 2, 2),                             # one count for 2 sequences
+        lambda: kvarn.decode_attn(q, kp, kp, nt.long(), 2, 4, 2, 2),
+        lambda: kvarn.decode_attn(q, kp, kp, nt, 2, 4, 2, 2, out=torch.zeros((2, 4, 128), dtype=f16)),
+        lambda: kvarn.decode_attn(q, kp, kp, nt, 2, 4, 2, 2, block_table=torch.zeros(15, dtype=i32)),
+        lambda: kvarn.decode_attn(q, kp, kp, nt, 2, 4, 2, 2, k_sink=torch.zeros((2, 2, 8, 128), dtype=f16)),
+        lambda: kvarn.decode_attn(q, kp, kp, nt, 2, 4, 2, 2, k_recent=torch.zeros((2, 2, 8, 128), dtype=f16),
+                                  v_recent=torch.zeros((2, 2, 8, 128), dtype=f16)),            # no n_recent
+        lambda: kvarn.decode_attn(q, kp, kp, nt, 2, 4, 2, 2, k_sink=torch.zeros((1, 2, 8, 128), dtype=f16),
+                                  v_sink=torch.zeros((1, 2, 8, 128), dtype=f16)),              # batch 1 of 2
+    ]
+    for i, call in enumerate(cases):
+        with pytest.raises(ValueError) as e:
+            call()
+        assert "device tensors" not in str(e.value), (i, str(e.value))
+    # the same calls with tensors of the right size get as far as the device check
+    for call in (lambda: kvarn.quantize_tiles(x, 2, 2, kvarn.AXIS_K, out=rec),
+                 lambda: kvarn.dequantize_tiles(rec, 2, 2, kvarn.AXIS_K, x),
+                 lambda: kvarn.decode_attn(q, kp, kp, nt, 2, 4, 2, 2, block_table=torch.zeros(16, dtype=i32))):
+        with pytest.raises(ValueError, match="device tensors"):
+            call()
