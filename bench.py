@@ -183,6 +183,44 @@ def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2, with_variant
     return dict(n_tiles_per_cache=n, bits=bits, wall_s=wall, per_op_ms=per_op, record_bytes=pb, variants=variants)
 
 
+def bench_other_workloads(reps=5):
+    """Per-launch rates of the codec on the two other cache shapes: the bulk
+    prefill (36 layers x 8 KV heads x 32768 tokens, dense, 2-bit K and V) and
+    the Phi-4-14B preset (40 layers x 10 KV heads x 8 sequences x 16384 tokens,
+    4-bit K, 2-bit V).  Whole caches, one launch per cache and op, HIP events
+    around each of `reps` launches after one untimed launch."""
+    dev = torch.device("cuda:0")
+    res = {}
+    for name, gen, bits_k, bits_v in (("prefill_qwen3_4b", synth.prefill, 2, 2),
+                                      ("phi4_14b_k4v2", synth.phi4, 4, 2)):
+        log(f"generating {name} inputs")
+        k, v = gen(device=dev)
+        n = k.numel() // (128 * 128)
+        out = torch.empty_like(k)
+        ops = {}
+        for cache, x, axis, bits in (("k", k, kvarn.AXIS_K, bits_k), ("v", v, kvarn.AXIS_V, bits_v)):
+            rec = torch.empty((n, kvarn.tile_bytes(bits)), dtype=torch.uint8, device=dev)
+            tq, td = OpTimer(), OpTimer()
+            for i in range(reps + 1):
+                fq = lambda: kvarn.quantize_tiles(x, n, bits, axis, out=rec)  # noqa: E731
+                fd = lambda: kvarn.dequantize_tiles(rec, n, bits, axis, out)  # noqa: E731
+                tq(fq) if i else fq()
+                td(fd) if i else fd()
+            alg = n * (32768 + kvarn.tile_bytes(bits))
+            for op, t in (("quantize_" + cache, tq.mean_ms()), ("dequantize_" + cache, td.mean_ms())):
+                ops[op] = {"bits": bits, "launch_ms": t, "tiles_per_s": n / (t * 1e-3),
+                           "fp16_equiv_GBs": n * 32768 / (t * 1e-3) / 1e9,
+                           "algorithmic_GBs": alg / (t * 1e-3) / 1e9,
+                           "frac_hbm": alg / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            del rec
+        total_ms = sum(o["launch_ms"] for o in ops.values())
+        res[name] = {"tiles_per_cache": n, "ops": ops,
+                     "quantize_plus_dequantize_fp16_equiv_GBs": 4 * n * 32768 / (total_ms * 1e-3) / 1e9}
+        del k, v, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def error_analysis(x: torch.Tensor, xd: torch.Tensor) -> dict:
     """Error statistics of dequantised key vectors xd against the originals x
     (rows = tokens, 128 channels), in float64.
@@ -548,6 +586,7 @@ def main():
     if not args.no_extras:
         line["variants_decode_append_k"] = codec["variants"]
         line["pages_context"] = pages_context(codec["variants"], q_ms)
+        line["other_workloads"] = bench_other_workloads()
     if not args.no_decode:
         line["decode_attn"] = bench_decode(args.decode_passes, 2, layers=args.decode_layers,
                                            with_windows=not args.no_extras)
