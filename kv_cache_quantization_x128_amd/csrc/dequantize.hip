@@ -166,6 +166,13 @@ __device__ __forceinline__ void store_segs8(void* __restrict__ out, const int64_
 // records; no change with the records in the memory-side cache).
 #define KVARN_ARGS_AT_ENTRY(...) asm volatile("" ::__VA_ARGS__)
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld16_nt(const uint8_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Raw bytes of one record as one lane reads them.
 struct RawRec {
     uint32_t wd[8];   // code words: K token rows row0 + i (channels 8cg..), V channel rows 8cg + i (tokens row0..)
@@ -180,6 +187,30 @@ struct RawRec {
 template <int BITS, int AXIS>
 __device__ __forceinline__ void load_rec(const uint8_t* __restrict__ rec, int row0, int cg, RawRec& r) {
     using R = Rec<BITS>;
+    if constexpr (BITS == 2 && AXIS == kAxisV) {
+        // 2-bit V: the lane's rows 8cg + 2q and 8cg + 2q + 1 at tokens row0..
+        // lie in the 16-byte chunk 1024 q + 16 (16 (row0 / 32) + cg) (bytes
+        // 2h, 2h + 1 and 8 + 2h, 9 + 2h with h = (row0 / 8) % 4), which the
+        // four lanes of a token quarter share: one 16-byte load per pair, 256
+        // contiguous bytes per wave and instruction, instead of two 2-byte loads
+        const int h = (row0 >> 3) & 3;
+        const uint32_t sel = (2u * (h & 1)) * 0x01010101u + 0x05040100u;   // bytes 2h', 2h'+1 of each dword
+        uint4 q4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) q4[q] = ld16_nt(rec + 1024 * q + 16 * (16 * (row0 >> 5) + cg));
+        const int g0 = row0, x0 = 8 * cg;
+        r.s1b = *reinterpret_cast<const uint2*>(rec + R::kS1 + g0);
+        r.zb = *reinterpret_cast<const uint4*>(rec + R::kZ + 2 * g0);
+        r.s2b = *reinterpret_cast<const uint2*>(rec + R::kS2 + x0);
+        __builtin_amdgcn_sched_barrier(0);   // keep every load above this point
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = (h & 2) ? q4[q].y : q4[q].x, hi = (h & 2) ? q4[q].w : q4[q].z;
+            r.wd[2 * q] = __builtin_amdgcn_perm(hi, lo, sel);   // row 2q in bits 0-15, row 2q + 1 in 16-31
+            r.wd[2 * q + 1] = 0u;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = (AXIS == kAxisK) ? row0 + i : 8 * cg + i;
@@ -318,12 +349,6 @@ __host__ __device__ constexpr uint32_t pos_bit_mask(int d, int q) {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 ld16_nt(const uint8_t* p) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 template <int BITS, int ODT>
 __global__ __launch_bounds__(256) void dequantize_k_mfma_kernel(const uint8_t* __restrict__ packed,
