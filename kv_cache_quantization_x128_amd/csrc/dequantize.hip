@@ -188,27 +188,37 @@ template <int BITS, int AXIS>
 __device__ __forceinline__ void load_rec(const uint8_t* __restrict__ rec, int row0, int cg, RawRec& r) {
     using R = Rec<BITS>;
     if constexpr (BITS == 2 && AXIS == kAxisV) {
-        // 2-bit V: the lane's rows 8cg + 2q and 8cg + 2q + 1 at tokens row0..
-        // lie in the 16-byte chunk 1024 q + 16 (16 (row0 / 32) + cg) (bytes
-        // 2h, 2h + 1 and 8 + 2h, 9 + 2h with h = (row0 / 8) % 4), which the
-        // four lanes of a token quarter share: one 16-byte load per pair, 256
-        // contiguous bytes per wave and instruction, instead of two 2-byte loads
-        const int h = (row0 >> 3) & 3;
-        const uint32_t sel = (2u * (h & 1)) * 0x01010101u + 0x05040100u;   // bytes 2h', 2h'+1 of each dword
-        uint4 q4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) q4[q] = ld16_nt(rec + 1024 * q + 16 * (16 * (row0 >> 5) + cg));
+        // 2-bit V: rows 8cg + 2q and 8cg + 2q + 1 of every token quarter h of
+        // the lane's tokens lie in the 16-byte chunk 1024 q + 16 (16 (row0 / 32)
+        // + cg), at bytes 2h', 2h' + 1 of dwords h/2 and 2 + h/2 (h' = h % 2).
+        // The lane of token quarter q loads chunk q (one load instruction, 1 KiB
+        // per wave in four 256-byte runs), cuts it into the four quarters'
+        // pieces, and a transpose over the four 16-lane rows (the quarters)
+        // hands every lane its own piece of each chunk.
+        const int q = (row0 >> 3) & 3;
+        const uint4 c = ld16_nt(rec + 1024 * q + 16 * (16 * (row0 >> 5) + cg));
         const int g0 = row0, x0 = 8 * cg;
         r.s1b = *reinterpret_cast<const uint2*>(rec + R::kS1 + g0);
         r.zb = *reinterpret_cast<const uint4*>(rec + R::kZ + 2 * g0);
         r.s2b = *reinterpret_cast<const uint2*>(rec + R::kS2 + x0);
         __builtin_amdgcn_sched_barrier(0);   // keep every load above this point
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = (h & 2) ? q4[q].y : q4[q].x, hi = (h & 2) ? q4[q].w : q4[q].z;
-            r.wd[2 * q] = __builtin_amdgcn_perm(hi, lo, sel);   // row 2q in bits 0-15, row 2q + 1 in 16-31
-            r.wd[2 * q + 1] = 0u;
-        }
+        // piece of quarter h: row 2q in bits 0-15, row 2q + 1 in bits 16-31
+        uint32_t p0 = __builtin_amdgcn_perm(c.z, c.x, 0x05040100u), p1 = __builtin_amdgcn_perm(c.z, c.x, 0x07060302u);
+        uint32_t p2 = __builtin_amdgcn_perm(c.w, c.y, 0x05040100u), p3 = __builtin_amdgcn_perm(c.w, c.y, 0x07060302u);
+        // p_h of lane row q -> p_q of lane row h.  permlane32_swap(a, b) leaves
+        // rows (a0, a1, b0, b1) in a and (a2, a3, b2, b3) in b; permlane16_swap(a, b)
+        // rows (a0, b0, a2, b2) in a and (a1, b1, a3, b3) in b.
+        auto sw32 = [](uint32_t& x, uint32_t& y) {
+            const auto t = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+            x = t[0], y = t[1];
+        };
+        auto sw16 = [](uint32_t& x, uint32_t& y) {
+            const auto t = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+            x = t[0], y = t[1];
+        };
+        sw32(p0, p2), sw32(p1, p3), sw16(p0, p1), sw16(p2, p3);
+        r.wd[0] = p0, r.wd[2] = p1, r.wd[4] = p2, r.wd[6] = p3;
+        r.wd[1] = r.wd[3] = r.wd[5] = r.wd[7] = 0u;
         return;
     }
 #pragma unroll
@@ -228,7 +238,7 @@ __device__ __forceinline__ void load_rec(const uint8_t* __restrict__ rec, int ro
 }
 
 template <int BITS, int AXIS, int ODT, bool ROT>
-__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ packed,
+__global__ __launch_bounds__(256, 5) void dequantize_kernel(const uint8_t* __restrict__ packed,
                                                          const int64_t* __restrict__ src_index,
                                                          void* __restrict__ out, int64_t tile_stride,
                                                          int64_t token_stride, const int64_t* __restrict__ dst_off) {
