@@ -29,13 +29,14 @@ TILE = kvarn.TILE
 
 class StreamingKVCache:
     def __init__(self, batch: int, n_kv_heads: int, max_tiles: int, bits_k: int = 2, bits_v: int = 2,
-                 n_sink: int = 128, recent_cap: int = TILE, flags: int = 0, device="cuda"):
+                 n_sink: int = 128, recent_cap: int = TILE, flags: int = 0, n_iter: int = 8, device="cuda"):
         if recent_cap != TILE:
             raise ValueError("the trailing window holds exactly one block (128 tokens) before it is quantised")
         if n_sink < 0 or batch <= 0 or n_kv_heads <= 0 or max_tiles <= 0:
             raise ValueError("bad cache shape")
         self.batch, self.n_kv_heads, self.max_tiles = batch, n_kv_heads, max_tiles
         self.bits_k, self.bits_v, self.n_sink, self.cap, self.flags = bits_k, bits_v, n_sink, recent_cap, flags
+        self.n_iter = n_iter   # normalisation rounds (0 with KVARN_NO_ROTATION: the KIVI records)
         dev = torch.device(device)
         f16 = dict(dtype=torch.float16, device=dev)
         self.sink_k = torch.zeros((batch, n_kv_heads, max(n_sink, 1), 128), **f16)
@@ -139,9 +140,9 @@ class StreamingKVCache:
         n = offs.numel()
         dst = torch.arange(self._next_record, self._next_record + n, device=offs.device, dtype=torch.int64)
         kvarn.quantize_tiles(self.recent_k, n, self.bits_k, kvarn.AXIS_K, tile_offset=offs, out=self.pool_k,
-                             dst_index=dst, flags=self.flags)
+                             dst_index=dst, n_iter=self.n_iter, flags=self.flags)
         kvarn.quantize_tiles(self.recent_v, n, self.bits_v, kvarn.AXIS_V, tile_offset=offs, out=self.pool_v,
-                             dst_index=dst, flags=self.flags)
+                             dst_index=dst, n_iter=self.n_iter, flags=self.flags)
         rows = torch.tensor([(bb * h + hh) * self.max_tiles + self._tiles[bb] for bb in seqs for hh in range(h)],
                             device=offs.device, dtype=torch.int64)
         self.block_table[rows] = dst.to(torch.int32)

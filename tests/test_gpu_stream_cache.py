@@ -28,8 +28,8 @@ def _oracle_attend(c, q):
                               v_recent=u16(c.recent_v), n_recent=c.n_recent.cpu().numpy())
 
 
-@pytest.mark.parametrize("bits_k,bits_v", [(2, 2), (4, 2)])
-def test_stream_cache_prefill_append_attend(dev, bits_k, bits_v):
+@pytest.mark.parametrize("bits_k,bits_v,flags,n_iter", [(2, 2, 0, 8), (4, 2, 0, 8), (2, 2, kvarn.NO_ROTATION, 0)])
+def test_stream_cache_prefill_append_attend(dev, bits_k, bits_v, flags, n_iter):
     batch, hkv, gs, max_tiles = 3, 2, 4, 5
     hq = hkv * gs
     g = torch.Generator(device=dev).manual_seed(123 + bits_k)
@@ -38,13 +38,14 @@ def test_stream_cache_prefill_append_attend(dev, bits_k, bits_v):
          torch.exp(0.5 * torch.randn((1, hkv, 1, 128), generator=g, device=dev))).half()
     v = torch.randn((batch, hkv, T, 128), generator=g, device=dev).half()
     q = torch.randn((batch, hq, 128), generator=g, device=dev).half()
-    c = StreamingKVCache(batch, hkv, max_tiles, bits_k, bits_v, device=dev)
+    c = StreamingKVCache(batch, hkv, max_tiles, bits_k, bits_v, flags=flags, n_iter=n_iter, device=dev)
     prompt = [128 + 2 * 128 + 30, 128 + 77, 128 + 128]
     c.prefill(k, v, lengths=prompt)
     assert [c.tokens(b) for b in range(batch)] == prompt
     assert c.n_tiles.tolist() == [2, 0, 1] and c.n_recent.tolist() == [30, 77, 0]
     # the body holds exactly what a direct quantisation of the same block gives
-    direct = kvarn.quantize(k[0, :, 128 + 128:128 + 256].contiguous(), bits_k, kvarn.AXIS_K)
+    direct = kvarn.quantize(k[0, :, 128 + 128:128 + 256].contiguous(), bits_k, kvarn.AXIS_K, n_iter=n_iter,
+                            flags=flags)
     rows = [(0 * hkv + h) * max_tiles + 1 for h in range(hkv)]
     rec = c.block_table[rows].long()
     assert torch.equal(c.pool_k[rec], direct)
