@@ -441,9 +441,10 @@ def copy_reference(reps=10, nbytes=1 << 28):
             "GBs": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(target_s=15.0, bits=2):
+def cpu_baseline(target_s=15.0, min_s=10.0, bits=2):
     """The oracle's quantise + dequantise of K and V tiles of the decode-append
-    workload (the whole step when it fits the time target), on the host."""
+    workload (the whole step when it fits the time target, repeated until at
+    least min_s of host time), on the host."""
     import oracle
 
     per_layer = 64 * 8
@@ -470,6 +471,10 @@ def cpu_baseline(target_s=15.0, bits=2):
     if n_layers > 1:
         bk, bv, offs = tiles(n_layers)
     dt = run(bk, bv, offs, m)
+    passes = 1
+    while m == 36 * per_layer and dt < min_s and passes < 4:
+        dt += run(bk, bv, offs, m)
+        passes += 1
     model = ""
     try:
         for ln in open("/proc/cpuinfo"):
@@ -479,10 +484,11 @@ def cpu_baseline(target_s=15.0, bits=2):
     except OSError:
         pass
     whole = " (the whole step)" if m == 36 * per_layer else ""
-    return {"value": 2 * (2 * m) * TILE_F16_BYTES / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+    times = f", {passes} passes" if passes > 1 else ""
+    return {"value": passes * 2 * (2 * m) * TILE_F16_BYTES / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle", "cpu_model": model, "cpus_in_affinity_mask": len(os.sched_getaffinity(0)),
             "sample": f"{m} K + {m} V tiles ({n_layers} layers) of the decode-append workload{whole}, quantise + "
-                      f"dequantise, {dt:.1f} s on the host"}
+                      f"dequantise{times}, {dt:.1f} s on the host"}
 
 
 def pages_context(variants, q_ms, layers=36):
