@@ -9,9 +9,11 @@
 //
 // Layout: one 256-thread workgroup per record; wave w owns tokens 32w..32w+31,
 // lane l = (rg = l/16, cg = l%16) the 8 x 8 block of tokens 32w + 8rg + a and
-// rotated-domain channels 8cg + j.  Each lane reads 8 code words of 16 (2-bit)
-// or 32 (4-bit) bits -- 8 token rows of K or 8 channel rows of V -- and widens
-// them with the gfx950 FP4 / FP8 converts (a 2-bit code c placed in an E2M1
+// rotated-domain channels 8cg + j.  Each lane needs 8 code words of 16 (2-bit)
+// or 32 (4-bit) bits -- 8 token rows of K or 8 channel rows of V; 2-bit V
+// records come in as one 16-byte load per lane and a transpose over the wave's
+// 16-lane rows, the others as one load per word -- and widens them with the
+// gfx950 FP4 / FP8 converts (a 2-bit code c placed in an E2M1
 // nibble reads as c/2, a 4-bit code in an E4M3 byte as c * 2^-9; the converts
 // scale both back exactly).  The rotation is three in-lane butterfly stages and
 // four stages across the 16 lanes of a DPP row; the lanes' input signs (folded
