@@ -225,6 +225,43 @@ def test_empty_batch_is_noop(dev):
     assert (out == 7).all()
 
 
+def test_codec_graph_replay_matches_eager(dev):
+    """Quantise then dequantise captured in a HIP graph (strided tiles through
+    tile offsets, records through a destination index): each of several replays,
+    with new tiles copied in and eager calls between them, gives the eager
+    records and tiles bit for bit (the launches allocate nothing and issue no
+    memset)."""
+    n, heads = 24, 3
+    g = torch.Generator(device=dev).manual_seed(31)
+    xs = [(torch.randn((2, 128, heads, 128), generator=g, device=dev) * 3).to(torch.bfloat16) for _ in range(4)]
+    x = xs[0].clone()
+    # 6 distinct tiles (2 sequences x 3 heads of the [seq][token][head][128] layout), each quantised 4 times
+    offs = torch.tensor([((i % 6) // heads) * 128 * heads * 128 + (i % heads) * 128 for i in range(6)] * 4,
+                        dtype=torch.int64, device=dev)
+    dst = torch.randperm(n, generator=g, device=dev)
+    rec = torch.empty((n, kvarn.tile_bytes(2)), dtype=torch.uint8, device=dev)
+    back = torch.empty((n, 128, 128), dtype=torch.bfloat16, device=dev)
+
+    def run():
+        kvarn.quantize_tiles(x, n, 2, V, token_stride=heads * 128, tile_offset=offs, out=rec, dst_index=dst)
+        kvarn.dequantize_tiles(rec, n, 2, V, back, src_index=dst)
+
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for i, xi in enumerate(xs):
+        x.copy_(xi)
+        graph.replay()
+        torch.cuda.synchronize()
+        got_rec, got_back = rec.clone(), back.clone()
+        run()                                     # eager, same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(got_rec, rec), i
+        assert torch.equal(got_back.view(torch.int16), back.view(torch.int16)), i
+
+
 def test_batch_larger_than_one_launch(dev):
     """A call with more than 2^23 tiles runs as several launches of at most 2^23
     tiles; tiles of the second launch are quantised and dequantised exactly like
