@@ -129,13 +129,22 @@ def _edge_tiles():
 
 @pytest.mark.parametrize("axis", [K, V])
 @pytest.mark.parametrize("bits", [2, 4])
-def test_edge_case_tiles(dev, axis, bits):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_edge_case_tiles(dev, axis, bits, dtype):
+    """Degenerate and extreme tiles through each input path: fp32 rotates with
+    the lane network, 16-bit inputs on the matrix cores."""
     tiles = _edge_tiles()
     names = list(tiles)
-    x = np.stack([tiles[n] for n in names])
-    _log("edge", names)
-    gpu = _gpu_quantize_dense(torch.from_numpy(x).to(dev), bits, axis)
-    rep = parity.compare_quantize(oracle.TileView.dense(x, oracle.DT_F32), bits, axis, gpu)
+    x32 = np.stack([tiles[n] for n in names])
+    xt = torch.from_numpy(x32).to(dtype)
+    _log("edge", dtype, names)
+    gpu = _gpu_quantize_dense(xt.to(dev), bits, axis)
+    if dtype == torch.float32:
+        view = oracle.TileView.dense(x32, oracle.DT_F32)
+    else:
+        view = oracle.TileView.dense(xt.view(torch.int16).numpy().view(np.uint16),
+                                     oracle.DT_BF16 if dtype == torch.bfloat16 else oracle.DT_F16)
+    rep = parity.compare_quantize(view, bits, axis, gpu)
     _log(rep)
     parity.assert_quantize_parity(rep, min_identical=0.999)
     out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), bits, axis, torch.float32).cpu().numpy()
