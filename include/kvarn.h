@@ -55,6 +55,12 @@
  *  - Argument errors are reported before any HIP call, so they can be checked
  *    on a machine without a GPU.  A failed kernel launch returns KVARN_EHIP.
  *  - Inputs must be finite; the output for non-finite input is unspecified.
+ *    Intermediate sums are fp32: |x| <= 2^50 for every element keeps them
+ *    finite.  The record's own formats bound what it represents: z saturates
+ *    at +-65504 (FP16) and s1, s2 are FP8 E4M3 in [2^-9, 448] (s2 after its
+ *    power-of-two gauge, so only the spread of the second scales counts);
+ *    groups beyond these ranges are still written, rounded as the oracle
+ *    rounds them, with a larger reconstruction error.
  */
 #ifndef KVARN_H
 #define KVARN_H
