@@ -152,6 +152,25 @@ def test_edge_case_tiles(dev, axis, bits, dtype):
     assert not out[0].any()  # the zero tile comes back exactly zero
 
 
+@pytest.mark.parametrize("shift", [-30, 30, 50])
+@pytest.mark.parametrize("axis", [K, V])
+def test_extreme_input_scales(dev, axis, shift):
+    """bf16 tiles scaled by 2^shift, up to the 2^50 the header allows: the same
+    decisions as the oracle, FP8 / FP16 saturation of s1 and z included, and
+    the dequantisation of those records."""
+    k, v = synth.tiny(seed=41)
+    x = torch.from_numpy((k if axis == K else v)[0, 0, :512].astype(np.float32) * np.float32(2.0 ** shift))
+    xb = x.reshape(4, 128, 128).to(torch.bfloat16)
+    gpu = _gpu_quantize_dense(xb.to(dev), 2, axis)
+    view = oracle.TileView.dense(xb.view(torch.int16).numpy().view(np.uint16), oracle.DT_BF16)
+    rep = parity.compare_quantize(view, 2, axis, gpu)
+    _log("scale 2^%d" % shift, rep)
+    parity.assert_quantize_parity(rep)
+    out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), 2, axis, torch.float32).cpu().numpy()
+    assert np.isfinite(out).all()
+    assert parity.dequant_fp32_error(out, oracle.dequantize(gpu, 2, axis)) < 1e-3
+
+
 @pytest.mark.parametrize("n_iter", [0, 1, 3, 20])
 def test_iteration_counts(dev, n_iter):
     k, _ = synth.tiny(seed=31)
