@@ -1,0 +1,48 @@
+"""Host-side pieces of bench.py that need no GPU: the algorithmic operation
+count behind the quantiser's roofline, the traffic record's staleness check,
+and the pages' context figure."""
+import json
+import os
+
+import pytest
+
+import bench
+from kv_cache_quantization_x128_amd import kvarn
+
+
+def test_quantize_flops_per_tile():
+    # per element: rotation 8 + 4 per normalisation half-step + metadata/codes 5
+    assert bench.quantize_flops_per_tile(kvarn.AXIS_K) == 16384 * (8 + 4 * 16 + 5)
+    assert bench.quantize_flops_per_tile(kvarn.AXIS_V) == 16384 * (8 + 4 * 15 + 5)
+    assert bench.quantize_flops_per_tile(kvarn.AXIS_V, n_iter=0) == 16384 * 13
+    assert bench.quantize_flops_per_tile(kvarn.AXIS_K, n_iter=4) == 16384 * (8 + 32 + 5)
+
+
+def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    rec = json.load(open(bench.TRAFFIC))
+    for kernel in bench.KERNEL_SOURCES:
+        k = rec["kernels"][kernel]
+        want = 1024 * (k["fetch_kib"] * rec["calibration"]["fetch_scale"] +
+                       k["write_kib"] * rec["calibration"]["write_scale"])
+        assert bench.measured_traffic(kernel) == pytest.approx(want), kernel
+    # any edit of a hashed source makes the record stale
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    for f in {f for fs in bench.KERNEL_SOURCES.values() for f in fs}:
+        (csrc / f).write_bytes(open(os.path.join(bench.CSRC, f), "rb").read())
+    monkeypatch.setattr(bench, "CSRC", str(csrc))
+    assert bench.measured_traffic("quantize") is not None
+    (csrc / "quantize.hip").write_bytes((csrc / "quantize.hip").read_bytes() + b"\n")
+    assert bench.measured_traffic("quantize") is None
+    assert bench.measured_traffic("decode_mfma") is not None
+    monkeypatch.setattr(bench, "TRAFFIC", str(tmp_path / "missing.json"))
+    assert bench.measured_traffic("decode_mfma") is None
+
+
+def test_pages_context_is_the_normalisation_share():
+    v = {"kvarn": {"quantize_k_ms": 0.5}, "hadamard_only": {"quantize_k_ms": 0.2}}
+    ctx = bench.pages_context(v, 0.47)
+    assert ctx["here_normalisation_ms"] == pytest.approx(0.3)
+    assert ctx["here_normalisation_per_layer_us"] == pytest.approx(300.0 / 36)
+    assert ctx["here_quantise_k_and_v_ms"] == pytest.approx(0.94)
+    assert "1.9 ms" in ctx["pages"] and "0.18 %" in ctx["pages"]
