@@ -292,10 +292,20 @@ __device__ __forceinline__ void load8_raw(const void* __restrict__ x, int64_t e0
     }
 }
 
+// The lane's index read from the hardware at each use (two VALU instructions):
+// the LDS addresses built from it are then not held in registers across the
+// normalisation loop, where the tile and its squares already take 128.
+__device__ __forceinline__ int hw_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // Sum of the four waves' partials in xch[buf][*][lane], fixed order (so every
 // wave holds bit-identical totals).
 template <class OP0, class OP1>
-__device__ __forceinline__ void cross_wave(Smem& sm, int buf, int w, int lane, const float (&z)[4], float (&t)[4]) {
+__device__ __forceinline__ void cross_wave(Smem& sm, int buf, int w, const float (&z)[4], float (&t)[4]) {
+    const int lane = hw_lane();
     sm.xch[buf][w][lane] = make_float4(z[0], z[1], z[2], z[3]);
     __syncthreads();
     const float4 p0 = sm.xch[buf][0][lane], p1 = sm.xch[buf][1][lane];
@@ -308,7 +318,8 @@ __device__ __forceinline__ void cross_wave(Smem& sm, int buf, int w, int lane, c
 
 // Per-lane column values for the lane's 8 columns, published by the owners
 // (lane (h, l) owns local columns 4h + 2l and 4h + 2l + 1) through the wave's LDS.
-__device__ __forceinline__ void col_bcast(Smem& sm, int w, int cg, int hl, float4 mine, float (&f)[8], float (&f2)[8]) {
+__device__ __forceinline__ void col_bcast(Smem& sm, int w, float4 mine, float (&f)[8], float (&f2)[8]) {
+    const int ln = hw_lane(), cg = ln & 15, hl = ln >> 4;
     sm.col[w][cg][hl] = mine;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -321,8 +332,9 @@ __device__ __forceinline__ void col_bcast(Smem& sm, int w, int cg, int hl, float
 
 // Per-lane row values for the lane's 8 rows, published by the row owners (lane
 // cg owns row a = 4 b3 + 2 b2 + b1; lanes cg and cg^1 write the same value).
-__device__ __forceinline__ void row_bcast(Smem& sm, int w, int rg, int a_own, float x, float x2, float (&f)[8],
-                                          float (&f2)[8]) {
+__device__ __forceinline__ void row_bcast(Smem& sm, int w, float x, float x2, float (&f)[8], float (&f2)[8]) {
+    const int ln = hw_lane(), rg = ln >> 4, cg = ln & 15;
+    const int a_own = 4 * ((cg >> 3) & 1) + 2 * ((cg >> 2) & 1) + ((cg >> 1) & 1);
     reinterpret_cast<float2*>(&sm.row[w][rg][0])[a_own] = make_float2(x, x2);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -335,8 +347,8 @@ __device__ __forceinline__ void row_bcast(Smem& sm, int w, int rg, int a_own, fl
 
 // Three workgroups per CU (at most 168 VGPRs): the tile and its squares take
 // 128 registers per lane, and the third workgroup hides the reduction and
-// barrier latencies of the other two.  The few long-lived addresses that no
-// longer fit are spilled once before the normalisation and reloaded after it.
+// barrier latencies of the other two.  The LDS exchange helpers read the lane
+// index from the hardware at each use, so that nothing is spilled.
 template <int BITS, int AXIS, int DT, bool ROT>
 __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
                                                           int64_t token_stride, const int64_t* __restrict__ tile_off,
@@ -474,7 +486,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             }
             float z[4];
             col_rs<OpSum, OpSum>(v, z);
-            cross_wave<OpSum, OpSum>(sm, buf, w, lane, z, t);
+            cross_wave<OpSum, OpSum>(sm, buf, w, z, t);
             buf ^= 1;
         }
         if (first) colsq[0] = t[1], colsq[1] = t[3];
@@ -484,7 +496,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         if (wave_any(mean[0] * mean[0] > kCancel * var[0] || mean[1] * mean[1] > kCancel * var[1])) {
             // exact centred second pass (uniform: every wave holds the same totals)
             float m8[8], unused[8];
-            col_bcast(sm, w, cg, hl, make_float4(mean[0], 0.0f, mean[1], 0.0f), m8, unused);
+            col_bcast(sm, w, make_float4(mean[0], 0.0f, mean[1], 0.0f), m8, unused);
             float v[16];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -498,7 +510,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             }
             float z[4], t2[4];
             col_rs<OpSum, OpSum>(v, z);
-            cross_wave<OpSum, OpSum>(sm, buf, w, lane, z, t2);
+            cross_wave<OpSum, OpSum>(sm, buf, w, z, t2);
             buf ^= 1;
             var[0] = t2[1] * kInvN, var[1] = t2[3] * kInvN;
         }
@@ -516,7 +528,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         float f[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) f[k] = step_factor(var[k], thr, floor2, fb);
-        col_bcast(sm, w, cg, hl, make_float4(sig * f[0], f[0] * f[0], sig * f[1], f[1] * f[1]), wc, wc2);
+        col_bcast(sm, w, make_float4(sig * f[0], f[0] * f[0], sig * f[1], f[1] * f[1]), wc, wc2);
         // rms of the token-step matrix: sum_j colsq_j * wc_j^2 / 128^2 (wave-local)
         const float rms2r = wave_sum(fmaf(colsq[0], f[0] * f[0], colsq[1] * (f[1] * f[1]))) * kInvNN;
 
@@ -540,7 +552,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         float rvar = fmaf(-rmean, rmean, rs[1] * kInvN);
         if (wave_any(rmean * rmean > kCancel * rvar)) {
             float m8[8], unused[8];
-            row_bcast(sm, w, rg, a_own, rmean, 0.0f, m8, unused);
+            row_bcast(sm, w, rmean, 0.0f, m8, unused);
             float v[16];
 #pragma unroll
             for (int a = 0; a < 8; ++a) {
@@ -559,7 +571,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         const float fbr = rms2r >= kDegAbs2 ? __builtin_amdgcn_rsqf(rms2r) : 1.0f;
         const float fr = step_factor(rvar, kDegRel2 * rms2r, kDegAbs2, fbr);
         last_rvar = rvar, last_rms2r = rms2r;
-        row_bcast(sm, w, rg, a_own, fr, fr * fr, wr, wr2);
+        row_bcast(sm, w, fr, fr * fr, wr, wr2);
     }
     if (AXIS == kAxisV && n_iter > 0) {
         float var[2], rms2;
@@ -594,7 +606,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         if ((cg & 1) == 0) rec[R::kS2 + row0 + a_own] = (uint8_t)code;
         const float m = __builtin_amdgcn_rcpf(fp8_decode_nonneg(code)) * kInvSqrtN;
         float m8[8], unused[8];
-        row_bcast(sm, w, rg, a_own, m, 0.0f, m8, unused);
+        row_bcast(sm, w, m, 0.0f, m8, unused);
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
             const float ma = sig * m8[a];                                // the reader's sign
@@ -612,7 +624,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         }
         float z[4], t[4];
         col_rs<OpMin, OpMax>(v, z);
-        cross_wave<OpMin, OpMax>(sm, buf, w, lane, z, t);
+        cross_wave<OpMin, OpMax>(sm, buf, w, z, t);
         float pub[4];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -627,7 +639,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1)) * (1.0f / kL);   // 1 / (L s1)
             pub[2 * k] = is1, pub[2 * k + 1] = -f16_bits_to_f32(zb) * is1;
         }
-        col_bcast(sm, w, cg, hl, make_float4(pub[0], pub[1], pub[2], pub[3]), inv_s1, zoff);
+        col_bcast(sm, w, make_float4(pub[0], pub[1], pub[2], pub[3]), inv_s1, zoff);
     } else {
         // gauge: mean of c over the 128 channels (every wave holds all of them)
         const float gmean = wave_sum(gc[0] + gc[1]) * kInvN;
@@ -644,7 +656,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             pub[2 * k + 1] = 0.0f;
         }
         float m8[8], unused[8];
-        col_bcast(sm, w, cg, hl, make_float4(pub[0], pub[1], pub[2], pub[3]), m8, unused);
+        col_bcast(sm, w, make_float4(pub[0], pub[1], pub[2], pub[3]), m8, unused);
 #pragma unroll
         for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -669,7 +681,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             *reinterpret_cast<uint16_t*>(rec + R::kZ + 2 * tok) = (uint16_t)zb;
         }
         const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1)) * (1.0f / kL);     // 1 / (L s1)
-        row_bcast(sm, w, rg, a_own, is1, -f16_bits_to_f32(zb) * is1, inv_s1, zoff);
+        row_bcast(sm, w, is1, -f16_bits_to_f32(zb) * is1, inv_s1, zoff);
     }
 
     // ---- 4. codes -------------------------------------------------------------------
