@@ -19,19 +19,30 @@ def test_quantize_flops_per_tile():
 
 
 def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
-    rec = json.load(open(bench.TRAFFIC))
-    for kernel in bench.KERNEL_SOURCES:
-        k = rec["kernels"][kernel]
-        want = 1024 * (k["fetch_kib"] * rec["calibration"]["fetch_scale"] +
-                       k["write_kib"] * rec["calibration"]["write_scale"])
-        assert bench.measured_traffic(kernel) == pytest.approx(want), kernel
-    # any edit of a hashed source makes the record stale
+    """A record whose source hashes match gives calibrated bytes; an edit of a
+    hashed source, or no record, gives None (the bench then reports no traffic)."""
+    import hashlib
+
     csrc = tmp_path / "csrc"
     csrc.mkdir()
     for f in {f for fs in bench.KERNEL_SOURCES.values() for f in fs}:
         (csrc / f).write_bytes(open(os.path.join(bench.CSRC, f), "rb").read())
+
+    def sha(kernel):
+        h = hashlib.sha256()
+        for f in bench.KERNEL_SOURCES[kernel]:
+            h.update((csrc / f).read_bytes())
+        return h.hexdigest()[:16]
+
+    rec = {"calibration": {"fetch_scale": 2.0, "write_scale": 1.0},
+           "kernels": {k: {"source_sha256_16": sha(k), "fetch_kib": 100.0 + i, "write_kib": 10.0}
+                       for i, k in enumerate(bench.KERNEL_SOURCES)}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "CSRC", str(csrc))
-    assert bench.measured_traffic("quantize") is not None
+    monkeypatch.setattr(bench, "TRAFFIC", str(path))
+    for i, k in enumerate(bench.KERNEL_SOURCES):
+        assert bench.measured_traffic(k) == pytest.approx(1024 * ((100.0 + i) * 2.0 + 10.0)), k
     (csrc / "quantize.hip").write_bytes((csrc / "quantize.hip").read_bytes() + b"\n")
     assert bench.measured_traffic("quantize") is None
     assert bench.measured_traffic("decode_mfma") is not None
