@@ -348,7 +348,8 @@ __device__ __forceinline__ void row_bcast(Smem& sm, int w, float x, float x2, fl
 // Three workgroups per CU (at most 168 VGPRs): the tile and its squares take
 // 128 registers per lane, and the third workgroup hides the reduction and
 // barrier latencies of the other two.  The LDS exchange helpers read the lane
-// index from the hardware at each use, so that nothing is spilled.
+// index from the hardware at each use, so that nothing is spilled (16-bit
+// inputs with the rotation; the other variants keep a few spilled values).
 template <int BITS, int AXIS, int DT, bool ROT>
 __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict__ x, int64_t tile_stride,
                                                           int64_t token_stride, const int64_t* __restrict__ tile_off,
