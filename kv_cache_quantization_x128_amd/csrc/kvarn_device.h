@@ -44,17 +44,8 @@ struct Rec {
 };
 
 // ---------------------------------------------------------------- conversions
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
     return __half2float(__ushort_as_half((unsigned short)h));
-}
-
-// Round to nearest even; inputs are finite.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
 }
 
 // Round to nearest even, saturating at +-65504.
@@ -106,150 +97,11 @@ __device__ __forceinline__ void fwht_regs(float (&v)[NV]) {
     }
 }
 
-// ---------------------------------------------------------------- lane reductions
-// DPP row operations (within each 16-lane row of a wave64).  The compiler fuses
-// the move into the consuming v_add/v_max/v_min (e.g. v_add_f32_dpp).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
+// ---------------------------------------------------------------- DPP controls
+// Row-local DPP lane patterns (within each 16-lane row of a wave64).
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each half row (xor 7)
 constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within the row (xor 15)
-
-// All-reduce over the 16 lanes of a row.  Each stage combines a lane with a
-// partner holding the same partial with operands swapped, and + / max / min
-// are commutative, so every lane ends with the bit-identical result.
-__device__ __forceinline__ float sum_lanes16(float v) {
-    v += dpp_mov<kDppXor1>(v);
-    v += dpp_mov<kDppXor2>(v);
-    v += dpp_mov<kDppHalfMirror>(v);
-    v += dpp_mov<kDppMirror>(v);
-    return v;
-}
-__device__ __forceinline__ float max_lanes16(float v) {
-    v = fmaxf(v, dpp_mov<kDppXor1>(v));
-    v = fmaxf(v, dpp_mov<kDppXor2>(v));
-    v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp_mov<kDppMirror>(v));
-    return v;
-}
-__device__ __forceinline__ float min_lanes16(float v) {
-    v = fminf(v, dpp_mov<kDppXor1>(v));
-    v = fminf(v, dpp_mov<kDppXor2>(v));
-    v = fminf(v, dpp_mov<kDppHalfMirror>(v));
-    v = fminf(v, dpp_mov<kDppMirror>(v));
-    return v;
-}
-
-// Value of lane (l ^ 16): ds_swizzle SWAP mode within 32-lane halves.
-__device__ __forceinline__ float xor16(float v) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-}
-// v[l] op v[l ^ 32] for every lane via v_permlane32_swap: with both operands v,
-// the two results hold (v[l], v[l^32]) in lane-independent order.
-__device__ __forceinline__ float sum_xor32(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-    return __int_as_float(r[0]) + __int_as_float(r[1]);
-}
-__device__ __forceinline__ float max_xor32(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
-}
-__device__ __forceinline__ float min_xor32(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-    return fminf(__int_as_float(r[0]), __int_as_float(r[1]));
-}
-// Sum / max / min over the 4 lanes that differ in lane bits 4-5.
-__device__ __forceinline__ float sum_lanes_hi(float v) {
-    v += xor16(v);
-    return sum_xor32(v);
-}
-__device__ __forceinline__ float max_lanes_hi(float v) {
-    v = fmaxf(v, xor16(v));
-    return max_xor32(v);
-}
-__device__ __forceinline__ float min_lanes_hi(float v) {
-    v = fminf(v, xor16(v));
-    return min_xor32(v);
-}
-
-// ---------------------------------------------------------------- tile row I/O
-// Load 64 consecutive elements starting at element e0 of x as fp32.
-template <int DT>
-__device__ __forceinline__ void load64(const void* __restrict__ x, int64_t e0, bool vec, float (&v)[64]) {
-    if constexpr (DT == kF32) {
-        const float* p = reinterpret_cast<const float*>(x) + e0;
-        if (vec) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float4 q = reinterpret_cast<const float4*>(p)[i];
-                v[4 * i] = q.x, v[4 * i + 1] = q.y, v[4 * i + 2] = q.z, v[4 * i + 3] = q.w;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 64; ++i) v[i] = p[i];
-        }
-    } else {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + e0;
-        if (vec) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint4 q = reinterpret_cast<const uint4*>(p)[i];
-                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    if constexpr (DT == kBF16) {
-                        v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
-                        v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-                    } else {
-                        v[8 * i + 2 * k] = f16_bits_to_f32(w[k] & 0xFFFFu);
-                        v[8 * i + 2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 64; ++i)
-                v[i] = (DT == kBF16) ? bf16_bits_to_f32(p[i]) : f16_bits_to_f32(p[i]);
-        }
-    }
-}
-
-// Store 64 fp32 values to consecutive elements starting at e0 as DT.
-template <int DT>
-__device__ __forceinline__ void store64(void* __restrict__ out, int64_t e0, bool vec, const float (&v)[64]) {
-    if constexpr (DT == kF32) {
-        float* p = reinterpret_cast<float*>(out) + e0;
-        if (vec) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 64; ++i) p[i] = v[i];
-        }
-    } else {
-        uint16_t* p = reinterpret_cast<uint16_t*>(out) + e0;
-        uint32_t h[64];
-#pragma unroll
-        for (int i = 0; i < 64; ++i) h[i] = (DT == kBF16) ? f32_to_bf16_bits(v[i]) : f32_to_f16_bits_sat(v[i]);
-        if (vec) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint4 q;
-                q.x = h[8 * i] | (h[8 * i + 1] << 16);
-                q.y = h[8 * i + 2] | (h[8 * i + 3] << 16);
-                q.z = h[8 * i + 4] | (h[8 * i + 5] << 16);
-                q.w = h[8 * i + 6] | (h[8 * i + 7] << 16);
-                reinterpret_cast<uint4*>(p)[i] = q;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 64; ++i) p[i] = (uint16_t)h[i];
-        }
-    }
-}
 
 }  // namespace kvarn

@@ -39,6 +39,23 @@ def nearest_fp8(x):
     return out
 
 
+def code_position(bits, axis, t, c):
+    """Byte and bit of the code of token t, channel c in the documented record
+    layout (include/kvarn.h): row r = s2 index, position p = group index."""
+    r, p = (t, c) if axis == 0 else (c, t)
+    n, i = r // 8, r % 8
+    if bits == 2:
+        return 1024 * (i // 2) + 16 * (16 * (p // 32) + n) + 8 * (i % 2) + (p % 32) // 4, 2 * (p % 4)
+    return 1024 * i + 16 * (16 * ((p // 16) % 4) + n) + 8 * (p // 64) + (p % 16) // 2, 4 * (p % 2)
+
+
+def set_code(record, bits, axis, t, c, code):
+    """Overwrite the code of token t, channel c of one packed record in place."""
+    byte, bit = code_position(bits, axis, t, c)
+    mask = (2 ** bits - 1) << bit
+    record[byte] = (int(record[byte]) & (0xFF ^ mask)) | ((int(code) << bit) & mask)
+
+
 def tiles_bits(tiles_f16):
     """float16 array [..., 128, 128] -> uint16 bits, flattened to [n][128][128]."""
     a = np.ascontiguousarray(np.asarray(tiles_f16, np.float16))

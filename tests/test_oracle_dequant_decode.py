@@ -9,20 +9,10 @@ import numpy as np
 import pytest
 import scipy.special
 
-from helpers import N, hadamard_ref, tiles_bits
+from helpers import N, code_position, hadamard_ref, tiles_bits
 from kv_cache_quantization_x128_amd import synth
 
 K, V = 0, 1
-
-
-def code_position(bits, axis, t, c):
-    """Byte and bit of the code of token t, channel c in the documented record
-    layout (include/kvarn.h): row r = s2 index, position p = group index."""
-    r, p = (t, c) if axis == K else (c, t)
-    n, i = r // 8, r % 8
-    if bits == 2:
-        return 1024 * (i // 2) + 16 * (16 * (p // 32) + n) + 8 * (i % 2) + (p % 32) // 4, 2 * (p % 4)
-    return 1024 * i + 16 * (16 * ((p // 16) % 4) + n) + 8 * (p // 64) + (p % 16) // 2, 4 * (p % 2)
 
 
 def _blank_record(orc, bits):

@@ -9,7 +9,7 @@ scales and an FP16 zero-point per 128 elements (paperlayer.ai summary, sections
 import numpy as np
 import pytest
 
-from helpers import N, hadamard_ref, nearest_fp8, rel_spread, tiles_bits
+from helpers import N, code_position, hadamard_ref, nearest_fp8, rel_spread, tiles_bits
 from kv_cache_quantization_x128_amd import synth
 
 K, V = 0, 1
@@ -258,8 +258,6 @@ def test_packing_layout(orc, axis):
     """Codes sit where include/kvarn.h documents them (rows along the s2 axis,
     chunks in the decode operand order), and every code bit of the block is
     used exactly once."""
-    from test_oracle_dequant_decode import code_position
-
     rng = np.random.default_rng(30 + axis)
     for bits in (2, 4):
         k, d, m, x = _grid_tile(rng, axis, bits, 1)
