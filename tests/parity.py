@@ -32,8 +32,12 @@ import oracle
 N = 128
 REL_META = 1e-4
 TIE_ABS = 1e-4
-TIE_REL32 = 4e-6
-ABS32 = 4e-6
+# Binary32 parts of the windows.  A binary32 model of the quantiser's own
+# operation order (emu32.py) strays from the oracle by at most ~0.22 of these on
+# the edge tiles and the workload samples (test_binary32_allowances.py), so the
+# window is about four times what the kernel's arithmetic can produce.
+TIE_REL32 = 1e-6
+ABS32 = 1.2e-6
 FP8_FLOOR = 2.0 ** -9
 
 
