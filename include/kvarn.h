@@ -85,7 +85,7 @@ extern "C" {
 enum {
     KVARN_OK = 0,
     KVARN_EINVAL = -1,       /* null pointer, negative size, bad enum value */
-    KVARN_EUNSUPPORTED = -2, /* bits not in {2, 4}, group not 128, > 8 query heads per KV head */
+    KVARN_EUNSUPPORTED = -2, /* bits not in {2, 4}, group not 128, a grid dimension out of range */
     KVARN_EALIGN = -3,       /* pointer or stride not aligned as documented */
     KVARN_EWORKSPACE = -4,   /* workspace smaller than kvarn_decode_attn_workspace_bytes */
     KVARN_EHIP = -5          /* the HIP runtime reported an error at launch */
@@ -197,9 +197,11 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
  *   n_tiles_per_seq device int32[batch]; values are clamped to [0, max_tiles]
  *   n_records       number of records in k_packed and in v_packed; table
  *                   entries outside [0, n_records) contribute nothing
- *   n_q_heads       multiple of n_kv_heads, at most 8 query heads per KV head;
- *                   batch at most 65535, and n_kv_heads times the number of
- *                   4-query chunks per KV head (1 or 2) at most 65535
+ *   n_q_heads       multiple of n_kv_heads (KVARN_EINVAL otherwise).  The
+ *                   query heads of one KV head are taken in chunks of 4, each
+ *                   chunk reading that head's records once.  batch at most
+ *                   65535, and n_kv_heads times the number of chunks per KV
+ *                   head, ceil(n_q_heads / n_kv_heads / 4), at most 65535
  *                   (KVARN_EUNSUPPORTED otherwise)
  *   bits_k, bits_v  2 or 4
  *   sm_scale        softmax scale, 1/sqrt(128) for standard attention; zero or

@@ -161,7 +161,7 @@ int kvarn_decode_attn_windows(const void* q, const void* k_packed, const void* v
     if (has_recent && (k_recent == nullptr || v_recent == nullptr || n_recent_per_seq == nullptr || recent_cap < 0 ||
                        recent_cap > 65536))
         return KVARN_EINVAL;
-    if (!valid_bits(bits_k) || !valid_bits(bits_v) || n_q_heads / n_kv_heads > 8) return KVARN_EUNSUPPORTED;
+    if (!valid_bits(bits_k) || !valid_bits(bits_v)) return KVARN_EUNSUPPORTED;
     // grid limits: z = batch, y = n_kv_heads x chunks of 4 query heads
     if (batch > 65535 || (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 3) / 4) > 65535) return KVARN_EUNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_packed) || !aligned16(v_packed) || !aligned16(out)) return KVARN_EALIGN;

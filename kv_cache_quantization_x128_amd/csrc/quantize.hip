@@ -44,7 +44,10 @@
 //                     note: the group-axis factor is absorbed into the group
 //                     scale).  For V the last token step is skipped: its result
 //                     is absorbed into s1 and never stored.
-//   4. RTN + pack     code = clamp(rint((Zn - z) / s1), 0, L); each lane packs
+//   4. RTN + pack     code = clamp(rint((Zn - z) / s1), 0, L), ties to even
+//                     (exact midpoints, common without the rotation, are kept
+//                     exact there: y = 16 X and a correctly rounded division);
+//                     each lane packs
 //                     8 codes of one code row (K: a token's 8 channels, V: a
 //                     channel's 8 tokens) into 16 (2-bit) or 32 (4-bit) bits
 //                     and stores them straight into the record.
@@ -58,7 +61,6 @@ namespace {
 
 constexpr float kInvN = 1.0f / 128.0f;
 constexpr float kInvNN = 1.0f / 16384.0f;
-constexpr float kSqrtN = 11.313708498984761f;       // sqrt(128)
 constexpr float kDegRel2 = 2.3283064365386963e-10f;  // (2^-16)^2: degenerate if var <= 2^-32 rms^2
 constexpr float kDegAbs2 = 7.52316384526264e-37f;    // 2^-120
 constexpr float kCancel = 16.0f;                     // mean^2 > 16 var: exact second pass
@@ -356,6 +358,10 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
                                                           int n_iter, uint8_t* __restrict__ packed,
                                                           const int64_t* __restrict__ dst_index) {
     constexpr bool rotate = ROT;   // false: KVARN_NO_ROTATION
+    // y = kYScale * Y: sqrt(128) from the unnormalised rotation, 16 without it
+    constexpr float kYScale2 = ROT ? 128.0f : 256.0f;                // kYScale^2
+    constexpr float kInvYScale2 = ROT ? kInvN : 1.0f / 256.0f;
+    constexpr float kInvYScale = ROT ? kInvSqrtN : 1.0f / 16.0f;
     using R = Rec<BITS>;
     __shared__ Smem sm;
 
@@ -378,13 +384,15 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
     float y[8][8];
     const bool vec = ((start | token_stride) & 7) == 0;
     if constexpr (!rotate) {
-        // the variant without the rotation: y = sqrt(128) X keeps the scaling
-        // the normalisation below expects of an unnormalised rotation
+        // the variant without the rotation: y = 16 X, a power of two, so that
+        // Zn = y * rcp(s2) / 16 is exact whenever s2 is a power of two (KIVI:
+        // s2 = 1/2); the normalisation is scale-free apart from the constants
+        // kYScale2 / kInvYScale below
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
             load8<DT>(x, start + (int64_t)(row0 + a) * token_stride + 8 * cg, vec, y[a]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) y[a][j] *= kSqrtN;
+            for (int j = 0; j < 8; ++j) y[a][j] *= 16.0f;
         }
     } else if constexpr (DT == kF32) {
 #pragma unroll
@@ -458,7 +466,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
 
     // ---- 2. dual-axis normalisation ---------------------------------------------------
     // Row factors wr = 1/r (per row, with squares wr2), column factors wc = sig/c'
-    // (c' = sqrt(128) c, the std of the stored scale) with squares wc2.
+    // (c' = kYScale c, the std of the stored scale) with squares wc2.
     float wr[8], wr2[8], wc[8], wc2[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) wr[k] = 1.0f, wr2[k] = 1.0f;
@@ -522,10 +530,10 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
     for (int it = 0; it < n_full; ++it) {
         float var[2], rms2;
         channel_moments(it == 0, var, rms2);
-        // degenerate rule on the stored scale (std floor 2^-60 * sqrt(128))
-        const float thr = kDegRel2 * rms2, floor2 = kDegAbs2 * 128.0f;
+        // degenerate rule on the stored scale (std floor 2^-60 * kYScale)
+        const float thr = kDegRel2 * rms2, floor2 = kDegAbs2 * kYScale2;
         const bool rms_ok = rms2 >= floor2;
-        const float fb = rms_ok ? __builtin_amdgcn_rsqf(rms2) : kInvSqrtN;
+        const float fb = rms_ok ? __builtin_amdgcn_rsqf(rms2) : kInvYScale;
         float f[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) f[k] = step_factor(var[k], thr, floor2, fb);
@@ -577,12 +585,13 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
     if (AXIS == kAxisV && n_iter > 0) {
         float var[2], rms2;
         channel_moments(n_iter == 1, var, rms2);
-        const float thr = kDegRel2 * rms2, floor2 = kDegAbs2 * 128.0f;
+        const float thr = kDegRel2 * rms2, floor2 = kDegAbs2 * kYScale2;
         const bool rms_ok = rms2 >= floor2;
-        // c of the owned columns, unscaled: sqrt(var / 128) or rms / sqrt(128)
+        // c of the owned columns, unscaled: sqrt(var) / kYScale or rms / kYScale
 #pragma unroll
         for (int k = 0; k < 2; ++k)
-            gc[k] = (var[k] > thr && var[k] >= floor2) ? sqrtf(var[k] * kInvN) : (rms_ok ? sqrtf(rms2 * kInvN) : 1.0f);
+            gc[k] = (var[k] > thr && var[k] >= floor2) ? sqrtf(var[k] * kInvYScale2)
+                                                       : (rms_ok ? sqrtf(rms2 * kInvYScale2) : 1.0f);
     }
     if (AXIS == kAxisK && n_iter > 0)   // r of the owned row after the last token step
         gr = (last_rvar > kDegRel2 * last_rms2r && last_rvar >= kDegAbs2)
@@ -591,6 +600,26 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
 
     // ---- 3. second scale, Zn, group statistics --------------------------------------
     constexpr float kL = (float)R::kL;
+    // (max - min) / L before its FP8 rounding: one multiply with the rotation,
+    // where the values carry full binary32 significands anyway; a correctly
+    // rounded division without it, where Zn keeps the inputs' short significands
+    auto group_range = [](float hi, float lo) {
+        if constexpr (rotate)
+            return (hi - lo) * (1.0f / kL);
+        else
+            return __fdiv_rn(hi - lo, kL);
+    };
+    // what the code step needs of a group: 1 / (L s1) and -z / (L s1) for one FMA
+    // per code with the rotation; s1 and z themselves without it (exact (Zn - z) / s1,
+    // so that an exact midpoint stays one and rounds to even like the oracle's)
+    auto code_params = [](uint32_t c1, uint32_t zb, float& p0, float& p1) {
+        if constexpr (rotate) {
+            const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1)) * (1.0f / kL);
+            p0 = is1, p1 = -f16_bits_to_f32(zb) * is1;
+        } else {
+            p0 = fp8_decode_nonneg(c1), p1 = f16_bits_to_f32(zb);
+        }
+    };
     const int64_t rec_idx = dst_index ? dst_index[tile] : tile;
     uint8_t* rec = packed + rec_idx * (int64_t)R::kBytes;
     float inv_s1[8], zoff[8];   // 1/(L s1) and -z/(L s1) per column (K) or per row (V) of this lane's block
@@ -605,7 +634,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         uint32_t code = fp8_encode_nonneg(gr * pow2f(-gexp));
         code = code < 1u ? 1u : code;                                    // floor 2^-9
         if ((cg & 1) == 0) rec[R::kS2 + row0 + a_own] = (uint8_t)code;
-        const float m = __builtin_amdgcn_rcpf(fp8_decode_nonneg(code)) * kInvSqrtN;
+        const float m = __builtin_amdgcn_rcpf(fp8_decode_nonneg(code)) * kInvYScale;
         float m8[8], unused[8];
         row_bcast(sm, w, m, 0.0f, m8, unused);
 #pragma unroll
@@ -629,7 +658,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         float pub[4];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            uint32_t c1 = fp8_encode_nonneg((t[2 * k + 1] - t[2 * k]) * (1.0f / kL));
+            uint32_t c1 = fp8_encode_nonneg(group_range(t[2 * k + 1], t[2 * k]));
             c1 = c1 < 1u ? 1u : c1;
             const uint32_t zb = f32_to_f16_bits_sat(t[2 * k]);
             const int ch = 8 * og + jc0 + k;
@@ -637,8 +666,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
                 rec[R::kS1 + ch] = (uint8_t)c1;
                 *reinterpret_cast<uint16_t*>(rec + R::kZ + 2 * ch) = (uint16_t)zb;
             }
-            const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1)) * (1.0f / kL);   // 1 / (L s1)
-            pub[2 * k] = is1, pub[2 * k + 1] = -f16_bits_to_f32(zb) * is1;
+            code_params(c1, zb, pub[2 * k], pub[2 * k + 1]);
         }
         col_bcast(sm, w, make_float4(pub[0], pub[1], pub[2], pub[3]), inv_s1, zoff);
     } else {
@@ -653,7 +681,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             uint32_t code = fp8_encode_nonneg(gc[k] * gs);
             code = code < 1u ? 1u : code;
             if (w == 0) rec[R::kS2 + 8 * og + jc0 + k] = (uint8_t)code;
-            pub[2 * k] = sig * __builtin_amdgcn_rcpf(fp8_decode_nonneg(code)) * kInvSqrtN;
+            pub[2 * k] = sig * __builtin_amdgcn_rcpf(fp8_decode_nonneg(code)) * kInvYScale;
             pub[2 * k + 1] = 0.0f;
         }
         float m8[8], unused[8];
@@ -673,7 +701,7 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
         }
         float z[2];
         row_rs<OpMin, OpMax>(v, cg, z);
-        uint32_t c1 = fp8_encode_nonneg((z[1] - z[0]) * (1.0f / kL));
+        uint32_t c1 = fp8_encode_nonneg(group_range(z[1], z[0]));
         c1 = c1 < 1u ? 1u : c1;
         const uint32_t zb = f32_to_f16_bits_sat(z[0]);
         if ((cg & 1) == 0) {
@@ -681,14 +709,17 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
             rec[R::kS1 + tok] = (uint8_t)c1;
             *reinterpret_cast<uint16_t*>(rec + R::kZ + 2 * tok) = (uint16_t)zb;
         }
-        const float is1 = __builtin_amdgcn_rcpf(fp8_decode_nonneg(c1)) * (1.0f / kL);     // 1 / (L s1)
-        row_bcast(sm, w, is1, -f16_bits_to_f32(zb) * is1, inv_s1, zoff);
+        float p0, p1;
+        code_params(c1, zb, p0, p1);
+        row_bcast(sm, w, p0, p1, inv_s1, zoff);
     }
 
     // ---- 4. codes -------------------------------------------------------------------
     // t = (Zn - z) / (L s1) clamped to [0, 1] (the clamp bit of the FMA), then
     // L t + 2^23 in one more FMA rounds L t to the nearest integer (ties to
-    // even) in the low mantissa bits: clamp(rint((Zn - z) / s1), 0, L).  Code rows follow the s2
+    // even) in the low mantissa bits: clamp(rint((Zn - z) / s1), 0, L).  Without
+    // the rotation (Zn - z) / s1 is a correctly rounded division instead, clamped
+    // to [0, L] before the 2^23 add.  Code rows follow the s2
     // axis: K packs the 8 channels of each of the lane's tokens (token rows), V
     // the 8 tokens of each of its channels (channel rows).  The shifted sums of
     // the 2^23 bit patterns are a constant, removed once per packed word.
@@ -705,8 +736,14 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(const void* __restrict
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int gi = (AXIS == kAxisK) ? j : a;
-            float t = __builtin_amdgcn_fmed3f(fmaf(y[a][j], inv_s1[gi], zoff[gi]), 0.0f, 1.0f);
-            t = fmaf(t, kL, kMagic);
+            float t;
+            if constexpr (rotate) {
+                t = __builtin_amdgcn_fmed3f(fmaf(y[a][j], inv_s1[gi], zoff[gi]), 0.0f, 1.0f);
+                t = fmaf(t, kL, kMagic);
+            } else {
+                // (Zn - z) / s1 correctly rounded: here inv_s1 holds s1 and zoff z
+                t = __builtin_amdgcn_fmed3f(__fdiv_rn(y[a][j] - zoff[gi], inv_s1[gi]), 0.0f, kL) + kMagic;
+            }
             if constexpr (AXIS == kAxisK)
                 word[a] += __float_as_uint(t) << (BITS * j);
             else

@@ -110,7 +110,8 @@ def test_decode_argument_errors():
     assert da(qp=None) == kvarn.EINVAL
     assert da(nt=None) == kvarn.EINVAL
     assert da(hq=6, hkv=4) == kvarn.EINVAL
-    assert da(hq=32, hkv=2) == kvarn.EUNSUPPORTED  # 16 query heads per KV head
+    assert da(b=0, hq=32, hkv=2) == kvarn.OK       # 16 query heads per KV head: four chunks of 4
+    assert da(hq=16 * 20000, hkv=20000) == kvarn.EUNSUPPORTED  # grid y: 20000 KV heads x 4 chunks
     assert da(bk=3) == kvarn.EUNSUPPORTED
     assert da(b=65536) == kvarn.EUNSUPPORTED                 # grid z
     assert da(hq=8 * 40000, hkv=40000) == kvarn.EUNSUPPORTED  # grid y: 40000 KV heads x 2 chunks

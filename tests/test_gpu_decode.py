@@ -37,7 +37,7 @@ def _run(dev, q, kr, vr, n_tiles, hkv, max_tiles, bk, bv, block_table=None):
     return out.float().cpu().numpy()
 
 
-@pytest.mark.parametrize("gs", [1, 2, 4, 8])
+@pytest.mark.parametrize("gs", [1, 2, 4, 6, 8, 16])
 @pytest.mark.parametrize("bk,bv", [(2, 2), (4, 2), (2, 4), (4, 4)])
 def test_decode_small_gqa_bits_ragged(dev, gs, bk, bv):
     batch, hkv, max_tiles = 3, 2, 3

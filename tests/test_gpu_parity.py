@@ -74,12 +74,11 @@ def test_variant_without_rotation(dev, n_iter, bits, axis, dtype):
     rep = parity.compare_quantize(view, bits, axis, gpu, n_iter=n_iter, rotate=False)
     _log(rep)
     # Without the rotation, Zn = X / s2 keeps the short significands of the
-    # 16-bit inputs (s2 and s1 are FP8 values, z an FP16 one), so (Zn - z) / s1
-    # lands exactly on a rounding midpoint far more often than for the method,
-    # whose rotated values mix 128 inputs.  Binary32 rounding decides those ties
-    # either way: every mismatch must still be an explained tie, but the raw
-    # identical rate is lower (0.06-0.11 % ties measured).
-    parity.assert_quantize_parity(rep, min_identical=0.998)
+    # 16-bit inputs, so (Zn - z) / s1 often lands exactly on a rounding
+    # midpoint.  The kernel forms it exactly there (power-of-two scaling, a
+    # correctly rounded division), so such a midpoint rounds to even as in the
+    # oracle: the method's 99.99 % bar holds.
+    parity.assert_quantize_parity(rep)
     out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), bits, axis, torch.float32, flags=kvarn.NO_ROTATION)
     ref = oracle.dequantize(gpu, bits, axis, rotate=False)
     assert parity.dequant_fp32_error(out.cpu().numpy(), ref) < 1e-3
