@@ -1,22 +1,27 @@
 """Throughput of the KVarN codec on one MI355X.
 
-One step = quantise + dequantise the whole decode-append batch of the Qwen3-4B
-shape: 36 layers x 64 sequences x 8 KV heads, one new 128-token block each, K
-and V in bf16 laid out token-major [layer][seq][token][head][128] -- 18432 K
-tiles and 18432 V tiles, 2-bit.  Inputs are resident in HBM before timing.
+Headline step = quantise + dequantise the whole KV cache of the Phi-4-14B
+preset: 40 layers x 10 KV heads x 8 sequences x 16384 tokens, head_dim 128,
+bf16 K and V (dense [layer][head][seq][token][128]), 4-bit keys and 2-bit
+values (the released kvarn_k4v2_g128 preset) -- 409600 K tiles and 409600 V
+tiles.  Inputs are resident in HBM before timing.
 
-value = fp16-equivalent bytes moved by the step (36864 tiles x 32 KiB in the
-quantiser + the same out of the dequantiser) / step time.  The roofline object
-describes the dominant kernel (the quantiser), which is bound by fp32 vector
-arithmetic: its algorithmic flops per launch (quantize_flops_per_tile) over its
-HIP-event-timed average launch duration, against the fp32 vector peak; its
-algorithmic HBM rate (tiles x (32768 + 4608) bytes) is reported beside it.
-Decode attention over the 2-bit cache (batch 16, 32 query heads on 8 KV heads,
-32768 tokens, 36 layers) is timed in the same run and reported in its own object.
-The oracle's quantise + dequantise is timed on a bounded sample on the host.
-Also in the line: the combined quantise + dequantise rate, a plain 256 MiB copy
-timed in the same run (the achievable-bandwidth reference), and the method
-variants on the K tiles (n_iter = 4 as a sensitivity row, Hadamard-only, KIVI).
+value = fp16-equivalent bytes moved by the step (819200 tiles x 32 KiB read by
+the quantiser + the same written by the dequantiser) / step time.  The
+roofline object describes the dominant kernel, the quantiser: algorithmic HBM
+bytes per launch (tiles x (32768 + record bytes)) over its mean launch time
+from HIP events around every launch (at least 20 per op), against 8 TB/s; the
+same launches' algorithmic fp32 rate against the non-packed fp32 vector peak
+is reported beside it.
+
+Also in the line, each timed in the same run: the codec on the decode-append
+block and on the bulk-prefill cache of the Qwen3-4B shape (secondary
+workloads), decode attention over the packed cache at the Qwen3-4B shape (2-bit
+K and V) and at the Phi-4 shape (4-bit K, 2-bit V), the method variants
+(n_iter = 4 sensitivity row, Hadamard-only, KIVI), the second scale's
+dequantisation cost, error statistics of the variants, a plain 256 MiB copy (the
+achievable-bandwidth reference), and the oracle timed on the host on a bounded
+sample of the headline workload plus a slice of one decode-attention layer.
 """
 from __future__ import annotations
 
@@ -51,9 +56,15 @@ def quantize_flops_per_tile(axis, n_iter=8):
     """
     half_steps = 2 * n_iter - (1 if axis == kvarn.AXIS_V and n_iter > 0 else 0)
     return 128 * 128 * (8 + 4 * half_steps + 5)
+
+
 CSRC = os.path.join(ROOT, "kv_cache_quantization_x128_amd", "csrc")
-TRAFFIC = os.path.join(ROOT, "profiles", "traffic_decode_append.json")
-KERNEL_SOURCES = {"quantize": ("quantize.hip", "kvarn_device.h"), "dequantize": ("dequantize.hip", "kvarn_device.h"),
+TRAFFIC = {"phi4": os.path.join(ROOT, "profiles", "traffic_phi4_k4v2.json"),
+           "decode_append": os.path.join(ROOT, "profiles", "traffic_decode_append.json")}
+KERNEL_SOURCES = {"quantize": ("quantize.hip", "kvarn_device.h"), "quantize_k": ("quantize.hip", "kvarn_device.h"),
+                  "quantize_v": ("quantize.hip", "kvarn_device.h"),
+                  "dequantize": ("dequantize.hip", "kvarn_device.h"), "dequantize_k": ("dequantize.hip", "kvarn_device.h"),
+                  "dequantize_v": ("dequantize.hip", "kvarn_device.h"),
                   "decode_mfma": ("decode_attn.hip", "kvarn_device.h")}
 
 
@@ -61,7 +72,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, workload="decode_append"):
     """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
     (scaled by the copy-kernel calibration), or None when the kernel's sources have
     changed since the counters were taken."""
@@ -69,7 +80,7 @@ def measured_traffic(kernel):
     import json as _json
 
     try:
-        rec = _json.load(open(TRAFFIC))
+        rec = _json.load(open(TRAFFIC[workload]))
         k = rec["kernels"][kernel]
         cal = rec["calibration"]
     except (OSError, KeyError, ValueError):
@@ -96,12 +107,83 @@ class OpTimer:
         e.record()
         self.pairs.append((s, e))
 
-    def mean_ms(self):
+    def times_ms(self):
         torch.cuda.synchronize()
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+    def mean_ms(self):
+        t = self.times_ms()
+        return float(np.mean(t)) if t else float("nan")
+
+    def stats(self):
+        t = self.times_ms()
+        return {"launches": len(t), "mean_ms": float(np.mean(t)), "median_ms": float(np.median(t)),
+                "min_ms": float(np.min(t)), "max_ms": float(np.max(t))}
 
 
-EVENT_EVERY = 10   # codec steps per step timed launch by launch
+EVENT_EVERY = 10   # decode-append codec steps per step timed launch by launch
+MIN_EVENTED = 20   # evented launches per op of the headline workload, whatever --steps is
+CPU_SAMPLE = 4096  # headline tiles per cache the host oracle is timed on
+
+PHI4 = dict(layers=40, heads=10, seqs=8, tokens=16384, bits_k=4, bits_v=2)
+
+
+def bench_phi4(steps, warmup):
+    """The headline step on the Phi-4-14B preset caches (see the module docstring).
+    HIP events bracket every launch of the timed steps (a launch takes
+    milliseconds, an event microseconds); when --steps is below MIN_EVENTED,
+    further evented steps follow the timed region so that every op has at least
+    MIN_EVENTED launch timings."""
+    dev = torch.device("cuda:0")
+    c = PHI4
+    log(f"generating the Phi-4 preset caches {c['layers']}x{c['heads']}x{c['seqs']}x{c['tokens']}x128 bf16")
+    k, v = synth.phi4(n_layers=c["layers"], n_heads=c["heads"], n_seq=c["seqs"], n_tokens=c["tokens"], device=dev)
+    n = k.numel() // (128 * 128)
+    bk, bv = c["bits_k"], c["bits_v"]
+    rk = torch.empty((n, kvarn.tile_bytes(bk)), dtype=torch.uint8, device=dev)
+    rv = torch.empty((n, kvarn.tile_bytes(bv)), dtype=torch.uint8, device=dev)
+    ok = torch.empty_like(k)
+    ov = torch.empty_like(v)
+    ops = (("quantize_k", lambda: kvarn.quantize_tiles(k, n, bk, kvarn.AXIS_K, out=rk)),
+           ("quantize_v", lambda: kvarn.quantize_tiles(v, n, bv, kvarn.AXIS_V, out=rv)),
+           ("dequantize_k", lambda: kvarn.dequantize_tiles(rk, n, bk, kvarn.AXIS_K, ok)),
+           ("dequantize_v", lambda: kvarn.dequantize_tiles(rv, n, bv, kvarn.AXIS_V, ov)))
+    timers = {name: OpTimer() for name, _ in ops}
+
+    def step(timed):
+        for name, fn in ops:
+            timers[name](fn) if timed else fn()
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {steps} headline steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for _ in range(max(0, MIN_EVENTED - steps)):
+        step(True)
+    per_op = {name: t.stats() for name, t in timers.items()}
+    # the seeded tile sample the host oracle is timed on: exact bf16 bytes of
+    # CPU_SAMPLE tiles of each cache, spread over layer, head and sequence
+    rng = np.random.default_rng(4)
+    sample = {}
+    for name, x in (("k", k), ("v", v)):
+        idx = torch.from_numpy(np.sort(rng.choice(n, size=CPU_SAMPLE, replace=False))).to(dev)
+        sample[name] = x.view(n, 128, 128)[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    alg = {"quantize_k": n * (TILE_F16_BYTES + kvarn.tile_bytes(bk)), "quantize_v": n * (TILE_F16_BYTES + kvarn.tile_bytes(bv))}
+    alg["dequantize_k"], alg["dequantize_v"] = alg["quantize_k"], alg["quantize_v"]
+    for name, st in per_op.items():
+        st["algorithmic_bytes_per_launch"] = alg[name]
+        st["algorithmic_GBs"] = alg[name] / (st["mean_ms"] * 1e-3) / 1e9
+        st["frac_hbm"] = st["algorithmic_GBs"] / HBM_PEAK_GBS
+        st["tiles_per_s"] = n / (st["mean_ms"] * 1e-3)
+        st["bits"] = bk if name.endswith("_k") else bv
+    del k, v, rk, rv, ok, ov
+    torch.cuda.empty_cache()
+    return dict(n_tiles_per_cache=n, wall_s=wall, per_op=per_op, sample=sample)
 
 
 def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2, with_variants=True):
@@ -184,15 +266,13 @@ def bench_codec(steps, warmup, layers=36, seqs=64, heads=8, bits=2, with_variant
 
 
 def bench_other_workloads(reps=5):
-    """Per-launch rates of the codec on the two other cache shapes: the bulk
-    prefill (36 layers x 8 KV heads x 32768 tokens, dense, 2-bit K and V) and
-    the Phi-4-14B preset (40 layers x 10 KV heads x 8 sequences x 16384 tokens,
-    4-bit K, 2-bit V).  Whole caches, one launch per cache and op, HIP events
-    around each of `reps` launches after one untimed launch."""
+    """Per-launch rates of the codec on the bulk-prefill cache of the Qwen3-4B
+    shape (36 layers x 8 KV heads x 32768 tokens, dense, 2-bit K and V).  Whole
+    caches, one launch per cache and op, HIP events around each of `reps`
+    launches after one untimed launch."""
     dev = torch.device("cuda:0")
     res = {}
-    for name, gen, bits_k, bits_v in (("prefill_qwen3_4b", synth.prefill, 2, 2),
-                                      ("phi4_14b_k4v2", synth.phi4, 4, 2)):
+    for name, gen, bits_k, bits_v in (("prefill_qwen3_4b", synth.prefill, 2, 2),):
         log(f"generating {name} inputs")
         k, v = gen(device=dev)
         n = k.numel() // (128 * 128)
@@ -315,15 +395,20 @@ def bench_app_i(contexts=(4096, 8192, 16384, 32768), heads=16, reps=20):
             "rows": rows}
 
 
-def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768, bits=2, with_windows=True):
+def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768, bits=2, bits_v=None,
+                 with_windows=True, seed=1005):
+    """Decode attention over packed caches of `layers` distinct layers (one
+    query token per sequence), 2-bit K and V by default, `bits_v` for other V
+    widths."""
     dev = torch.device("cuda:0")
     nt = tokens // 128
-    g = synth.generator(1005, dev)
+    bk, bv = bits, (bits if bits_v is None else bits_v)
+    g = synth.generator(seed, dev)
     caches = []
-    log(f"building {layers} decode-attention layers (batch {batch}, {tokens} tokens)")
+    log(f"building {layers} decode-attention layers (batch {batch}, {hq}/{hkv} heads, {tokens} tokens, K{bk}V{bv})")
     for _ in range(layers):
         q, k, v = synth.decode_attn_layer(g, n_seq=batch, n_kv_heads=hkv, n_q_heads=hq, n_tokens=tokens, device=dev)
-        caches.append((q, kvarn.quantize(k, bits, kvarn.AXIS_K), kvarn.quantize(v, bits, kvarn.AXIS_V)))
+        caches.append((q, kvarn.quantize(k, bk, kvarn.AXIS_K), kvarn.quantize(v, bv, kvarn.AXIS_V)))
         del k, v
     torch.cuda.empty_cache()
     n_tiles = torch.full((batch,), nt, dtype=torch.int32, device=dev)
@@ -333,7 +418,7 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
 
     def one_pass(timed):
         for q, kr, vr in caches:
-            fn = lambda: kvarn.decode_attn(q, kr, vr, n_tiles, hkv, nt, bits, bits, out=out, workspace=ws)  # noqa
+            fn = lambda: kvarn.decode_attn(q, kr, vr, n_tiles, hkv, nt, bk, bv, out=out, workspace=ws)  # noqa
             timer(fn) if timed else fn()
 
     # eager: HIP events around every call (includes the host's launch overhead
@@ -368,19 +453,19 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
         raise RuntimeError("decode attention: graph replay differs from the eager pass")
     del graph
 
-    pb = kvarn.tile_bytes(bits)
-    alg_bytes = 2 * batch * hkv * nt * pb + 2 * batch * hq * 128 * 2
+    alg_bytes = batch * hkv * nt * (kvarn.tile_bytes(bk) + kvarn.tile_bytes(bv)) + 2 * batch * hq * 128 * 2
     ach = alg_bytes / (layer_ms * 1e-3) / 1e9
     res = {
         "workload": f"decode attention: batch {batch}, {hq} query heads on {hkv} KV heads, head_dim 128, "
-                    f"{tokens}-token {bits}-bit K/V cache, {layers} layers",
+                    f"{tokens}-token cache, {bk}-bit K, {bv}-bit V, {layers} layers",
         "layer_ms": layer_ms,
         "timing": f"HIP events around {passes} replays of a HIP graph holding the {layers}-layer pass",
         "eager_layer_ms": eager_ms,
         "eager_wall_s_per_pass": wall / passes,
         "fp16_equiv_GBs": 2 * batch * hkv * nt * TILE_F16_BYTES / (layer_ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode_mfma"),
+                     "frac": ach / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("decode_mfma") if (bk, bv, batch, hq, hkv, tokens) == (2, 2, 16, 32, 8, 32768) else None,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "tokens_per_s": batch * hq / (layer_ms * 1e-3),
     }
@@ -399,7 +484,7 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
 
     def window_pass():
         for (q, kr, vr), (ks, vs, kt, vt) in zip(caches, wins):
-            kvarn.decode_attn(q, kr, vr, n_tiles, hkv, nt, bits, bits, out=out, workspace=ws, k_sink=ks, v_sink=vs,
+            kvarn.decode_attn(q, kr, vr, n_tiles, hkv, nt, bk, bv, out=out, workspace=ws, k_sink=ks, v_sink=vs,
                               k_recent=kt, v_recent=vt, n_recent=n_recent)
 
     window_pass()
@@ -441,40 +526,7 @@ def copy_reference(reps=10, nbytes=1 << 28):
             "GBs": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(target_s=15.0, min_s=10.0, bits=2):
-    """The oracle's quantise + dequantise of K and V tiles of the decode-append
-    workload (the whole step when it fits the time target, repeated until at
-    least min_s of host time), on the host."""
-    import oracle
-
-    per_layer = 64 * 8
-
-    def tiles(n_layers):
-        k, v = synth.decode_append(n_layers=n_layers, n_seq=64, n_heads=8, device="cpu")
-        offs = synth.decode_append_offsets(n_layers, 64, 8, device="cpu").numpy()
-        bits16 = lambda x: x.contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1)  # noqa: E731
-        return bits16(k), bits16(v), offs
-
-    def run(bk, bv, offs, m):
-        t0 = time.perf_counter()
-        for buf, axis in ((bk, oracle.AXIS_K), (bv, oracle.AXIS_V)):
-            view = oracle.TileView(buf, oracle.DT_BF16, m, token_stride=8 * 128, offsets=offs[:m])
-            rec = oracle.quantize(view, bits, axis)
-            oracle.dequantize(rec, bits, axis)
-        return time.perf_counter() - t0
-
-    bk, bv, offs = tiles(1)
-    probe = 64
-    dt = run(bk, bv, offs, probe)
-    m = int(min(36 * per_layer, max(probe, probe * target_s / max(dt, 1e-3))))
-    n_layers = -(-m // per_layer)
-    if n_layers > 1:
-        bk, bv, offs = tiles(n_layers)
-    dt = run(bk, bv, offs, m)
-    passes = 1
-    while m == 36 * per_layer and dt < min_s and passes < 4:
-        dt += run(bk, bv, offs, m)
-        passes += 1
+def host_info():
     model = ""
     try:
         for ln in open("/proc/cpuinfo"):
@@ -483,12 +535,59 @@ def cpu_baseline(target_s=15.0, min_s=10.0, bits=2):
                 break
     except OSError:
         pass
-    whole = " (the whole step)" if m == 36 * per_layer else ""
-    times = f", {passes} passes" if passes > 1 else ""
+    return {"cpu_model": model, "cpus_in_affinity_mask": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(sample, n_full, min_s=10.0, max_passes=4):
+    """The oracle's quantise + dequantise of the headline workload's seeded tile
+    sample (CPU_SAMPLE K tiles at 4 bits + CPU_SAMPLE V tiles at 2 bits, the
+    exact bf16 bytes of the GPU's inputs), repeated until at least min_s of host
+    work, in the headline's unit (fp16-equivalent GB/s of quantise + dequantise);
+    the whole step's host time is extrapolated from it."""
+    import oracle
+
+    def one_pass():
+        t0 = time.perf_counter()
+        for key, axis, bits in (("k", oracle.AXIS_K, PHI4["bits_k"]), ("v", oracle.AXIS_V, PHI4["bits_v"])):
+            rec = oracle.quantize(oracle.TileView.dense(sample[key], oracle.DT_BF16), bits, axis)
+            oracle.dequantize(rec, bits, axis)
+        return time.perf_counter() - t0
+
+    dt, passes = one_pass(), 1
+    while dt < min_s and passes < max_passes:
+        dt += one_pass()
+        passes += 1
+    m = sample["k"].shape[0]
+    per_pass = dt / passes
     return {"value": passes * 2 * (2 * m) * TILE_F16_BYTES / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "cpu_model": model, "cpus_in_affinity_mask": len(os.sched_getaffinity(0)),
-            "sample": f"{m} K + {m} V tiles ({n_layers} layers) of the decode-append workload{whole}, quantise + "
-                      f"dequantise{times}, {dt:.1f} s on the host"}
+            "kind": "oracle", **host_info(),
+            "sample": f"{m} K tiles (4-bit) + {m} V tiles (2-bit) of the Phi-4 preset caches (seeded, over layer, head "
+                      f"and sequence), quantise + dequantise, {passes} passes, {dt:.1f} s on the host",
+            "extrapolated_step_s": per_pass * n_full / m,
+            "extrapolation": f"the whole headline step ({n_full} K + {n_full} V tiles) at the sample's rate"}
+
+
+def cpu_decode_layer(n_seq_sample=2, batch=16, hq=32, hkv=8, tokens=32768):
+    """The oracle's decode attention on a slice of one layer of the Qwen3-4B
+    decode workload (n_seq_sample of the batch's sequences, all their KV heads
+    and tiles; records written by the oracle itself, untimed), extrapolated to
+    the whole layer."""
+    import oracle
+
+    g = synth.generator(1005, "cpu")
+    q, k, v = synth.decode_attn_layer(g, n_seq=n_seq_sample, n_kv_heads=hkv, n_q_heads=hq, n_tokens=tokens,
+                                      device="cpu")
+    bits16 = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1, 128, 128)  # noqa: E731
+    kr = oracle.quantize(oracle.TileView.dense(bits16(k), oracle.DT_BF16), 2, oracle.AXIS_K)
+    vr = oracle.quantize(oracle.TileView.dense(bits16(v), oracle.DT_BF16), 2, oracle.AXIS_V)
+    nt = tokens // 128
+    t0 = time.perf_counter()
+    oracle.decode_attn(q.numpy().view(np.uint16), kr, vr, np.full(n_seq_sample, nt, np.int32), hq, hkv, nt, 2, 2)
+    dt = time.perf_counter() - t0
+    return {"layer_s": dt * batch / n_seq_sample, "unit": "s per layer", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_seq_sample} of {batch} sequences x {hkv} KV heads x {tokens} tokens (2-bit K and V), "
+                      f"{dt:.1f} s on the host, extrapolated to the layer's {batch} sequences"}
 
 
 def pages_context(variants, q_ms, layers=36):
@@ -510,17 +609,19 @@ def pages_context(variants, q_ms, layers=36):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-passes", type=int, default=20)
     ap.add_argument("--decode-layers", type=int, default=36)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the decode-append and prefill codec workloads")
     ap.add_argument("--copy-calib", action="store_true",
                     help="time the plain 256 MiB device copy 10 times instead of 5 (counter calibration runs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the method variants, the FP16-window decode, the KIVI comparison and the error "
-                         "analysis (counter runs: every dispatch of a kernel is then the headline workload's)")
+                         "analysis (counter runs: every dispatch of a kernel is then a listed workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the codec has no cross-GPU step); got --gpus {args.gpus}",
@@ -529,41 +630,26 @@ def main():
     kvarn.load()
     torch.cuda.init()
 
-    codec = bench_codec(args.steps, args.warmup, with_variants=not args.no_extras)
-    n = codec["n_tiles_per_cache"]
-    per_op = codec["per_op_ms"]
-    step_ms = codec["wall_s"] / args.steps * 1e3
+    head = bench_phi4(args.steps, args.warmup)
+    n = head["n_tiles_per_cache"]
+    per_op = head["per_op"]
+    step_ms = head["wall_s"] / args.steps * 1e3
     f16_bytes = 2 * (2 * n) * TILE_F16_BYTES          # quantiser reads + dequantiser writes, K and V
     value = f16_bytes / (step_ms * 1e-3) / 1e9
-    pb = codec["record_bytes"]
-    q_ms = 0.5 * (per_op["quantize_k"] + per_op["quantize_v"])
-    dq_ms = 0.5 * (per_op["dequantize_k"] + per_op["dequantize_v"])
-    dqc_ms = per_op["dequantize_cold"]
-    q_alg = n * (TILE_F16_BYTES + pb)
-    q_ach = q_alg / (q_ms * 1e-3) / 1e9
-    dq_ach = q_alg / (dq_ms * 1e-3) / 1e9
-    # the quantiser is bound by fp32 vector arithmetic (the normalisation sweeps),
-    # not by HBM: its roofline is algorithmic flops per launch over launch time
-    q_flops = n * 0.5 * (quantize_flops_per_tile(kvarn.AXIS_K) + quantize_flops_per_tile(kvarn.AXIS_V))
-    q_tflops = q_flops / (q_ms * 1e-3) / 1e12
-    ops = {
-        "quantize": {"launch_ms": q_ms, "tiles_per_launch": n, "tiles_per_s": n / (q_ms * 1e-3),
-                     "algorithmic_GBs": q_ach, "frac_hbm": q_ach / HBM_PEAK_GBS,
-                     "algorithmic_TFLOPs": q_tflops, "frac_fp32_vector_peak": q_tflops / FP32_VECTOR_PEAK_TFLOPS,
-                     "fp16_equiv_GBs": n * TILE_F16_BYTES / (q_ms * 1e-3) / 1e9},
-        "dequantize": {"launch_ms": dq_ms, "tiles_per_launch": n, "tiles_per_s": n / (dq_ms * 1e-3),
-                       "algorithmic_GBs": dq_ach, "frac_hbm": dq_ach / HBM_PEAK_GBS,
-                       "fp16_equiv_GBs": n * TILE_F16_BYTES / (dq_ms * 1e-3) / 1e9,
-                       "traffic": measured_traffic("dequantize"),
-                       "note": "inside the step: records written by the preceding quantise launches"},
-        "combined": {"what": "quantise + dequantise of the same tiles: algorithmic bytes of both over the sum of "
-                             "their launch times", "GBs": 2 * q_alg / ((q_ms + dq_ms) * 1e-3) / 1e9,
-                     "frac_hbm": 2 * q_alg / ((q_ms + dq_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "dequantize_cold": {"launch_ms": dqc_ms, "tiles_per_s": n / (dqc_ms * 1e-3),
-                            "algorithmic_GBs": q_alg / (dqc_ms * 1e-3) / 1e9,
-                            "frac_hbm": q_alg / (dqc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                            "note": "records evicted from the memory-side cache before each launch"},
-    }
+    qk = per_op["quantize_k"]
+    q_flops = n * quantize_flops_per_tile(kvarn.AXIS_K)
+    q_tflops = q_flops / (qk["mean_ms"] * 1e-3) / 1e12
+    ops = dict(per_op)
+    t_q = per_op["quantize_k"]["mean_ms"] + per_op["quantize_v"]["mean_ms"]
+    t_dq = per_op["dequantize_k"]["mean_ms"] + per_op["dequantize_v"]["mean_ms"]
+    b_q = per_op["quantize_k"]["algorithmic_bytes_per_launch"] + per_op["quantize_v"]["algorithmic_bytes_per_launch"]
+    ops["combined"] = {"what": "quantise + dequantise of the K and V caches: algorithmic bytes of all four launches over "
+                               "the sum of their mean launch times",
+                       "GBs": 2 * b_q / ((t_q + t_dq) * 1e-3) / 1e9,
+                       "frac_hbm": 2 * b_q / ((t_q + t_dq) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "fp16_equiv_GBs": 4 * n * TILE_F16_BYTES / ((t_q + t_dq) * 1e-3) / 1e9}
+    for name in ("quantize_k", "quantize_v", "dequantize_k", "dequantize_v"):
+        ops[name]["traffic"] = measured_traffic(name, "phi4")
     line = {
         "metric": "KV quantize+dequant GB/s (fp16-equiv) and % of HBM peak on 1 MI355X",
         "value": value,
@@ -576,32 +662,67 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded N(0,1), outlier channels x15, 5% outlier tokens x4, RoPE-rotated keys; bf16)",
-        "config": {"workload": "decode_append: Qwen3-4B KV shape, 36 layers x 64 sequences x 8 KV heads, one "
-                               "128-token block each, head_dim 128, bf16 K and V, 2-bit",
-                   "tiles_per_step": 2 * n, "layout": "[layer][seq][token][head][128]", "n_iter": 8},
+        "data": "synthetic (seeded N(0,1), 3 outlier channels x20 per (layer, head), 5% outlier tokens x4, "
+                "RoPE-rotated keys; bf16)",
+        "config": {"workload": "Phi-4-14B KV preset kvarn_k4v2_g128: 40 layers x 10 KV heads x 8 sequences x 16384 "
+                               "tokens, head_dim 128, bf16 K and V, 4-bit K and 2-bit V",
+                   "tiles_per_step": 2 * n, "layout": "[layer][head][seq][token][128]", "n_iter": 8,
+                   "input_dtype": "bf16", "records": "4-bit K 8704 B, 2-bit V 4608 B per tile"},
         "frac_of_hbm_peak": value / HBM_PEAK_GBS,
-        "roofline": {"bound": "alu", "kernel": "quantize_kernel", "achieved": q_tflops,
-                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": q_tflops / FP32_VECTOR_PEAK_TFLOPS,
-                     "peak_non_packed_fp32": FP32_NONPACKED_PEAK_TFLOPS,
-                     "frac_non_packed_fp32": q_tflops / FP32_NONPACKED_PEAK_TFLOPS,
-                     "traffic": measured_traffic("quantize"), "algorithmic_flops_per_launch": q_flops,
-                     "algorithmic_bytes_per_launch": q_alg, "hbm_GBs": q_ach, "hbm_frac": q_ach / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": "quantize_kernel<4, K, bf16, rotation> (the 409600 K tiles)",
+                     "achieved": qk["algorithmic_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": qk["algorithmic_GBs"] / HBM_PEAK_GBS, "traffic": ops["quantize_k"]["traffic"],
+                     "algorithmic_bytes_per_launch": qk["algorithmic_bytes_per_launch"],
+                     "launch_ms_mean": qk["mean_ms"], "launch_ms_median": qk["median_ms"],
+                     "launches_timed": qk["launches"],
+                     "alu": {"what": "the same launches' algorithmic fp32 operations (quantize_flops_per_tile) against "
+                                     "the non-packed fp32 vector peak (the library is built without packed fp32)",
+                             "achieved_TFLOPs": q_tflops, "peak_TFLOPs": FP32_NONPACKED_PEAK_TFLOPS,
+                             "frac": q_tflops / FP32_NONPACKED_PEAK_TFLOPS,
+                             "algorithmic_flops_per_launch": q_flops}},
         "ops": ops,
     }
-    if not args.no_extras:
-        line["variants_decode_append_k"] = codec["variants"]
-        line["pages_context"] = pages_context(codec["variants"], q_ms)
-        line["other_workloads"] = bench_other_workloads()
+    sample = head.pop("sample")
+    if not args.no_secondary:
+        codec = bench_codec(args.steps * 10, args.warmup * 3, with_variants=not args.no_extras)
+        m = codec["n_tiles_per_cache"]
+        pc = codec["per_op_ms"]
+        sec_ms = codec["wall_s"] / (args.steps * 10) * 1e3
+        q_ms = 0.5 * (pc["quantize_k"] + pc["quantize_v"])
+        dq_ms = 0.5 * (pc["dequantize_k"] + pc["dequantize_v"])
+        alg = m * (TILE_F16_BYTES + codec["record_bytes"])
+        line["decode_append"] = {
+            "workload": "Qwen3-4B KV shape, 36 layers x 64 sequences x 8 KV heads, one new 128-token block each, "
+                        "bf16 token-major [layer][seq][token][head][128], 2-bit K and V",
+            "tiles_per_step": 2 * m, "ms_per_step": sec_ms,
+            "fp16_equiv_GBs": 2 * (2 * m) * TILE_F16_BYTES / (sec_ms * 1e-3) / 1e9,
+            "quantize": {"launch_ms": q_ms, "algorithmic_GBs": alg / (q_ms * 1e-3) / 1e9,
+                         "frac_hbm": alg / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "tiles_per_s": m / (q_ms * 1e-3),
+                         "traffic": measured_traffic("quantize")},
+            "dequantize": {"launch_ms": dq_ms, "algorithmic_GBs": alg / (dq_ms * 1e-3) / 1e9,
+                           "frac_hbm": alg / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "traffic": measured_traffic("dequantize"),
+                           "note": "inside the step: records written by the preceding quantise launches"},
+            "dequantize_cold": {"launch_ms": pc["dequantize_cold"],
+                                "frac_hbm": alg / (pc["dequantize_cold"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "note": "records evicted from the memory-side cache before each launch"},
+        }
+        if not args.no_extras:
+            line["variants_decode_append_k"] = codec["variants"]
+            line["pages_context"] = pages_context(codec["variants"], q_ms)
+            line["other_workloads"] = bench_other_workloads()
     if not args.no_decode:
         line["decode_attn"] = bench_decode(args.decode_passes, 2, layers=args.decode_layers,
                                            with_windows=not args.no_extras)
+        line["decode_attn_phi4_k4v2"] = bench_decode(args.decode_passes, 2, layers=40, batch=8, hq=40, hkv=10,
+                                                     tokens=16384, bits=4, bits_v=2, with_windows=False, seed=1007)
         if not args.no_extras:
             line["dequant_overhead_vs_kivi"] = bench_app_i()
             line["error_analysis"] = bench_error_analysis()
     line["copy_reference"] = copy_reference(reps=10 if args.copy_calib else 5)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+        line["cpu_baseline"] = cpu_baseline(sample, n)
+        line["cpu_baseline_decode_layer"] = cpu_decode_layer()
     print(json.dumps(line), flush=True)
 
 

@@ -10,12 +10,24 @@ import bench
 from kv_cache_quantization_x128_amd import kvarn
 
 
-def test_quantize_flops_per_tile():
-    # per element: rotation 8 + 4 per normalisation half-step + metadata/codes 5
-    assert bench.quantize_flops_per_tile(kvarn.AXIS_K) == 16384 * (8 + 4 * 16 + 5)
-    assert bench.quantize_flops_per_tile(kvarn.AXIS_V) == 16384 * (8 + 4 * 15 + 5)
-    assert bench.quantize_flops_per_tile(kvarn.AXIS_V, n_iter=0) == 16384 * 13
-    assert bench.quantize_flops_per_tile(kvarn.AXIS_K, n_iter=4) == 16384 * (8 + 32 + 5)
+def test_quantize_flops_per_tile_against_the_survey_count():
+    """The roofline's operation count against an independent count of one
+    128 x 128 tile: the rotation's butterflies (7 stages of 16384 add/sub) plus
+    the 1/sqrt(128) scale (16384 multiplies), 0.13 M; each normalisation
+    half-step two matrix-vector products with the tile (the weighted sums of Y
+    and of Y^2, one multiply-add = 2 flops per element each), 16 half-steps of
+    2 x 16384 FMAs = 0.52 M FMAs for K; metadata and codes about 0.07 M.  The
+    exact figure may differ from the estimate only in the ~0.07 M term."""
+    rotation = 7 * 16384 + 16384
+    half_step = 2 * 16384 * 2
+    for axis, half_steps in ((kvarn.AXIS_K, 16), (kvarn.AXIS_V, 15)):
+        est = rotation + half_steps * half_step + 70_000
+        assert abs(bench.quantize_flops_per_tile(axis) - est) <= 0.02 * est
+    # n_iter = 0 leaves the rotation and the codes only
+    assert abs(bench.quantize_flops_per_tile(kvarn.AXIS_K, n_iter=0) - (rotation + 70_000)) <= 15_000
+    # eight iterations cost twice the normalisation of four
+    k8, k4, k0 = (bench.quantize_flops_per_tile(kvarn.AXIS_K, n_iter=t) for t in (8, 4, 0))
+    assert k8 - k0 == 2 * (k4 - k0)
 
 
 def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
@@ -40,13 +52,13 @@ def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(tmp_path, m
     path = tmp_path / "traffic.json"
     path.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "CSRC", str(csrc))
-    monkeypatch.setattr(bench, "TRAFFIC", str(path))
+    monkeypatch.setattr(bench, "TRAFFIC", {"decode_append": str(path)})
     for i, k in enumerate(bench.KERNEL_SOURCES):
         assert bench.measured_traffic(k) == pytest.approx(1024 * ((100.0 + i) * 2.0 + 10.0)), k
     (csrc / "quantize.hip").write_bytes((csrc / "quantize.hip").read_bytes() + b"\n")
     assert bench.measured_traffic("quantize") is None
     assert bench.measured_traffic("decode_mfma") is not None
-    monkeypatch.setattr(bench, "TRAFFIC", str(tmp_path / "missing.json"))
+    monkeypatch.setattr(bench, "TRAFFIC", {"decode_append": str(tmp_path / "missing.json")})
     assert bench.measured_traffic("decode_mfma") is None
 
 

@@ -143,25 +143,46 @@ def test_decode_block_table_empty_and_out_of_range(dev):
     assert parity.rel_l2_rows(got_bad[2, gs:2 * gs], ref_two[0]).max() <= TOL
 
 
-def test_decode_attention_full_size(dev):
-    """Qwen3-4B shape: batch 16, 32 query heads on 8 KV heads, 32768-token 2-bit
-    caches (256 tiles per sequence) quantised on the GPU with planted peaked keys;
-    the whole layer (all 16 x 32 output rows) checked against the oracle."""
-    g = synth.generator(1005, dev)
-    q, k, v = synth.decode_attn_layer(g, device=dev)
+def _oracle_layer_records(k, v, bits_k, bits_v):
+    """Records of a whole decode layer written by the oracle from the exact bf16
+    bytes of the GPU tensors k, v [seq][kv head][tokens][128] (so the expected
+    output depends on nothing the HIP path computed)."""
+    kb = parity.bits_of(k).reshape(-1, 128, 128)
+    vb = parity.bits_of(v).reshape(-1, 128, 128)
+    kr = oracle.quantize(oracle.TileView.dense(kb, oracle.DT_BF16), bits_k, K)
+    vr = oracle.quantize(oracle.TileView.dense(vb, oracle.DT_BF16), bits_v, V)
+    return kr, vr
+
+
+@pytest.mark.parametrize("shape", ["qwen3_4b_k2v2", "phi4_14b_k4v2"])
+def test_decode_attention_full_layer(dev, shape):
+    """A whole decode layer against the oracle, on records the oracle wrote:
+    Qwen3-4B shape (batch 16, 32 query heads on 8 KV heads, 32768-token 2-bit
+    K and V caches) and the Phi-4-14B preset shape (batch 8, 40 query heads on
+    10 KV heads, 16384 tokens, 4-bit K, 2-bit V), with planted peaked keys; all
+    output rows checked."""
+    if shape == "qwen3_4b_k2v2":
+        g = synth.generator(1005, dev)
+        q, k, v = synth.decode_attn_layer(g, device=dev)
+        bk, bv = 2, 2
+    else:
+        g = synth.generator(1007, dev)
+        q, k, v = synth.decode_attn_layer(g, n_seq=8, n_kv_heads=10, n_q_heads=40, n_tokens=16384, device=dev)
+        bk, bv = 4, 2
     B, Hkv, T = k.shape[0], k.shape[1], k.shape[2]
     nt = T // 128
-    kr = kvarn.quantize(k, 2, K)
-    vr = kvarn.quantize(v, 2, V)
+    _log(shape, "oracle quantises", 2 * B * Hkv * nt, "tiles")
+    kr, vr = _oracle_layer_records(k, v, bk, bv)
+    del k, v
     n_tiles = torch.full((B,), nt, dtype=torch.int32, device=dev)
-    out = kvarn.decode_attn(q, kr, vr, n_tiles, Hkv, nt, 2, 2)
+    out = kvarn.decode_attn(q, torch.from_numpy(kr).to(dev), torch.from_numpy(vr).to(dev), n_tiles, Hkv, nt, bk, bv)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     assert np.isfinite(got).all()
-    ref = oracle.decode_attn(parity.bits_of(q), kr.cpu().numpy(), vr.cpu().numpy(), np.full(B, nt, np.int32),
-                             q.shape[1], Hkv, nt, 2, 2)
+    _log(shape, "oracle decode")
+    ref = oracle.decode_attn(parity.bits_of(q), kr, vr, np.full(B, nt, np.int32), q.shape[1], Hkv, nt, bk, bv)
     err = parity.rel_l2_rows(got, ref)
-    _log("full-size decode max rel l2", err.max(), "mean", err.mean())
+    _log(shape, "full-layer decode max rel l2", err.max(), "mean", err.mean())
     assert err.max() <= TOL
 
 
@@ -301,11 +322,27 @@ def test_streaming_cache_block_fill(dev):
     q = rng.standard_normal((batch, hq, 128)).astype(np.float16)
     checks = 0
 
+    def oracle_pools():
+        """The pools as the oracle writes them: tile j of (b, h) is tokens
+        n_sink + 128 j ... of that head, at the record the block table names."""
+        ok_, ov_ = np.zeros((pool_k.shape[0], pb), np.uint8), np.zeros((pool_k.shape[0], pb), np.uint8)
+        tab, nts = table.cpu().numpy(), n_tiles.cpu().numpy()
+        for b in range(batch):
+            for h in range(hkv):
+                for j in range(int(nts[b])):
+                    r = int(tab[(b * hkv + h) * max_tiles + j])
+                    t0 = n_sink + 128 * j
+                    for pool, x, axis in ((ok_, kx, K), (ov_, vx, V)):
+                        pool[r] = oracle.quantize(oracle.TileView.dense(u16(x[b, h, t0:t0 + 128]), oracle.DT_F16),
+                                                  2, axis)[0]
+        return ok_, ov_
+
     def check(tag):
         out = kvarn.decode_attn(d(q), pool_k, pool_v, n_tiles, hkv, max_tiles, 2, 2, block_table=table,
                                 k_sink=sink_k, v_sink=sink_v, k_recent=rec_k, v_recent=rec_v, n_recent=n_recent)
         torch.cuda.synchronize()
-        ref = oracle.decode_attn(u16(q), pool_k.cpu().numpy(), pool_v.cpu().numpy(), n_tiles.cpu().numpy(), hq, hkv,
+        opk, opv = oracle_pools()
+        ref = oracle.decode_attn(u16(q), opk, opv, n_tiles.cpu().numpy(), hq, hkv,
                                  max_tiles, 2, 2, block_table=table.cpu().numpy(),
                                  k_sink=u16(sink_k.cpu().numpy()), v_sink=u16(sink_v.cpu().numpy()),
                                  k_recent=u16(rec_k.cpu().numpy()), v_recent=u16(rec_v.cpu().numpy()),

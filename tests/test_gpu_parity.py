@@ -25,6 +25,17 @@ def _log(*a):
     print(*a, flush=True)
 
 
+def _check_dequant(dev, rec, bits, axis, rotate=True):
+    """fp32 dequantisation of records written by the oracle, against the
+    oracle's dequantisation of the same records (within 1e-3 x tile RMS)."""
+    flags = 0 if rotate else kvarn.NO_ROTATION
+    out = kvarn.dequantize(torch.from_numpy(rec).to(dev), bits, axis, torch.float32, flags=flags).cpu().numpy()
+    err = parity.dequant_fp32_error(out, oracle.dequantize(rec, bits, axis, rotate=rotate))
+    _log("dequant max err / tile rms", err)
+    assert err < 1e-3
+    return out
+
+
 def _gpu_quantize_dense(x_dev, bits, axis, n_iter=8):
     rec = kvarn.quantize(x_dev, bits, axis, n_iter=n_iter)
     torch.cuda.synchronize()
@@ -43,10 +54,8 @@ def test_tiny_quantize_and_dequantize(dev, bits, axis):
     rep = parity.compare_quantize(view, bits, axis, gpu)
     _log(rep)
     parity.assert_quantize_parity(rep)
-    # dequantise the GPU's own records: fp32 against the oracle's dequantisation of them
-    out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), bits, axis, torch.float32).cpu().numpy()
-    ref = oracle.dequantize(gpu, bits, axis)
-    assert parity.dequant_fp32_error(out, ref) < 1e-3
+    # dequantise the oracle's records: fp32 against the oracle's dequantisation of them
+    _check_dequant(dev, oracle.quantize(view, bits, axis), bits, axis)
 
 
 # ------------------------------------------------------------------------------------- variants
@@ -79,9 +88,7 @@ def test_variant_without_rotation(dev, n_iter, bits, axis, dtype):
     # correctly rounded division), so such a midpoint rounds to even as in the
     # oracle: the method's 99.99 % bar holds.
     parity.assert_quantize_parity(rep)
-    out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), bits, axis, torch.float32, flags=kvarn.NO_ROTATION)
-    ref = oracle.dequantize(gpu, bits, axis, rotate=False)
-    assert parity.dequant_fp32_error(out.cpu().numpy(), ref) < 1e-3
+    _check_dequant(dev, oracle.quantize(view, bits, axis, n_iter=n_iter, rotate=False), bits, axis, rotate=False)
 
 
 # ------------------------------------------------------------------------------------- dequant
@@ -146,8 +153,7 @@ def test_edge_case_tiles(dev, axis, bits, dtype):
     rep = parity.compare_quantize(view, bits, axis, gpu)
     _log(rep)
     parity.assert_quantize_parity(rep, min_identical=0.999)
-    out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), bits, axis, torch.float32).cpu().numpy()
-    assert parity.dequant_fp32_error(out, oracle.dequantize(gpu, bits, axis)) < 1e-3
+    out = _check_dequant(dev, oracle.quantize(view, bits, axis), bits, axis)
     assert not out[0].any()  # the zero tile comes back exactly zero
 
 
@@ -165,9 +171,8 @@ def test_extreme_input_scales(dev, axis, shift):
     rep = parity.compare_quantize(view, 2, axis, gpu)
     _log("scale 2^%d" % shift, rep)
     parity.assert_quantize_parity(rep)
-    out = kvarn.dequantize(torch.from_numpy(gpu).to(dev), 2, axis, torch.float32).cpu().numpy()
+    out = _check_dequant(dev, oracle.quantize(view, 2, axis), 2, axis)
     assert np.isfinite(out).all()
-    assert parity.dequant_fp32_error(out, oracle.dequantize(gpu, 2, axis)) < 1e-3
 
 
 @pytest.mark.parametrize("n_iter", [0, 1, 3, 20])
@@ -352,9 +357,11 @@ def _check_tiles(x_flat, offsets, token_stride, rec, bits, axis, idx, tag, chunk
                 total[k] += rep[k]
             total["raw_identical_codes"] = (total["raw_identical_codes"] * n_before +
                                             rep["raw_identical_codes"] * rep["tiles"]) / total["tiles"]
-        d = ci[torch.linspace(0, ci.numel() - 1, min(n_deq, ci.numel()), device=ci.device).long()]
-        out = kvarn.dequantize(rec[d].contiguous(), bits, axis, torch.float32).cpu().numpy()
-        deq_err = max(deq_err, parity.dequant_fp32_error(out, oracle.dequantize(rec[d].cpu().numpy(), bits, axis)))
+        # dequantisation of the oracle's records of n_deq of the chunk's tiles
+        d = np.linspace(0, ci.numel() - 1, min(n_deq, ci.numel())).astype(np.int64)
+        orec = oracle.quantize(oracle.TileView.dense(tiles[d], oracle.DT_BF16), bits, axis)
+        out = kvarn.dequantize(torch.from_numpy(orec).to(x_flat.device), bits, axis, torch.float32).cpu().numpy()
+        deq_err = max(deq_err, parity.dequant_fp32_error(out, oracle.dequantize(orec, bits, axis)))
         _log(tag, f"tiles {c0 + ci.numel()}/{idx.numel()}", rep)
     _log(tag, "total", total, "dequant max err / tile rms", deq_err)
     parity.assert_quantize_parity(total)

@@ -19,10 +19,30 @@ def _log(*a):
     print(*a, flush=True)
 
 
-def _oracle_attend(c, q):
+def _oracle_pools(c, hist_k, hist_v, n_sink=128):
+    """The record pools as the oracle writes them from the tokens each sequence
+    received (hist_*[b]: fp16 [n_kv_heads][tokens][128] in arrival order): tile j
+    of (b, h) is tokens n_sink + 128 j ... at the record the block table names."""
+    pk = np.zeros(tuple(c.pool_k.shape), np.uint8)
+    pv = np.zeros(tuple(c.pool_v.shape), np.uint8)
+    tab, nts = c.block_table.cpu().numpy(), c.n_tiles.cpu().numpy()
+    for b in range(len(hist_k)):
+        for h in range(c.n_kv_heads):
+            for j in range(int(nts[b])):
+                r = int(tab[(b * c.n_kv_heads + h) * c.max_tiles + j])
+                t0 = n_sink + 128 * j
+                for pool, hist, axis, bits in ((pk, hist_k, kvarn.AXIS_K, c.bits_k), (pv, hist_v, kvarn.AXIS_V, c.bits_v)):
+                    x = np.ascontiguousarray(hist[b][h, t0:t0 + 128]).view(np.uint16)
+                    pool[r] = oracle.quantize(oracle.TileView.dense(x, oracle.DT_F16), bits, axis,
+                                              n_iter=c.n_iter, rotate=not c.flags)[0]
+    return pk, pv
+
+
+def _oracle_attend(c, q, hist_k, hist_v):
     u16 = lambda t: t.contiguous().cpu().numpy().view(np.uint16)  # noqa: E731
     hq = q.shape[1]
-    return oracle.decode_attn(u16(q), c.pool_k.cpu().numpy(), c.pool_v.cpu().numpy(), c.n_tiles.cpu().numpy(), hq,
+    pk, pv = _oracle_pools(c, hist_k, hist_v)
+    return oracle.decode_attn(u16(q), pk, pv, c.n_tiles.cpu().numpy(), hq,
                               c.n_kv_heads, c.max_tiles, c.bits_k, c.bits_v, block_table=c.block_table.cpu().numpy(),
                               rotate=not c.flags, k_sink=u16(c.sink_k), v_sink=u16(c.sink_v), k_recent=u16(c.recent_k),
                               v_recent=u16(c.recent_v), n_recent=c.n_recent.cpu().numpy())
@@ -50,6 +70,8 @@ def test_stream_cache_prefill_append_attend(dev, bits_k, bits_v, flags, n_iter):
     rec = c.block_table[rows].long()
     assert torch.equal(c.pool_k[rec], direct)
     pos = list(prompt)
+    hist_k = [k[b, :, :prompt[b]].cpu().numpy() for b in range(batch)]     # tokens received, per sequence
+    hist_v = [v[b, :, :prompt[b]].cpu().numpy() for b in range(batch)]
     fills = 0
     for step in range(180):
         active = [b for b in range(batch) if not (b == 1 and step % 3 == 0)]   # sequence 1 skips some steps
@@ -59,11 +81,13 @@ def test_stream_cache_prefill_append_attend(dev, bits_k, bits_v, flags, n_iter):
         c.append(kt, vt, active=active)
         for b in active:
             pos[b] += 1
+            hist_k[b] = np.concatenate([hist_k[b], kt[b].cpu().numpy()[:, None]], axis=1)
+            hist_v[b] = np.concatenate([hist_v[b], vt[b].cpu().numpy()[:, None]], axis=1)
         if c.n_tiles.tolist() != tiles_before or step == 179:
             fills += c.n_tiles.tolist() != tiles_before
             got = c.attend(q).float().cpu().numpy()
             torch.cuda.synchronize()
-            err = parity.rel_l2_rows(got, _oracle_attend(c, q))
+            err = parity.rel_l2_rows(got, _oracle_attend(c, q, hist_k, hist_v))
             _log("stream cache", bits_k, bits_v, "step", step, "tiles", c.n_tiles.tolist(), "recent",
                  c.n_recent.tolist(), "max rel l2", err.max())
             assert err.max() <= TOL
