@@ -246,6 +246,26 @@ int kvarn_decode_attn_windows(const void *q, const void *k_packed, const void *v
                               const void *v_recent, const int32_t *n_recent_per_seq, int recent_cap, void *out,
                               void *workspace, size_t workspace_bytes, int flags, hipStream_t stream);
 
+/*
+ * kvarn_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results as kvarn_decode_attn, with the split-K
+ * partials in a device array of KVARN_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on (for the life of the process) instead of a
+ * caller workspace.  The call allocates nothing; the caller still passes q,
+ * the records and out.  Arguments as for kvarn_decode_attn; a shape whose
+ * kvarn_decode_attn_workspace_bytes exceeds KVARN_NOALLOC_SCRATCH_BYTES is
+ * refused with KVARN_EWORKSPACE before any HIP call.  All calls on one GPU
+ * share that GPU's array: calls that overlap in time on one GPU (on different
+ * streams, or from different host threads without ordering) race and give
+ * undefined results.  The array's contents on entry do not matter.
+ */
+#define KVARN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int kvarn_decode_attn_noalloc(const void *q, const void *k_packed, const void *v_packed, const int32_t *block_table,
+                              const int32_t *n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
+                              int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, void *out,
+                              int flags, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

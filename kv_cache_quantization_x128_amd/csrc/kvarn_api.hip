@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvarn.h"
 #include "kvarn_launch.h"
@@ -42,6 +43,39 @@ int check_tiles(const void* buf, int64_t n_tiles, int64_t tile_stride, int64_t t
     if (!aligned16(buf)) return KVARN_EALIGN;
     if ((token_stride & 7) != 0 || (offs == nullptr && (tile_stride & 7) != 0)) return KVARN_EALIGN;
     if (offs != nullptr && (reinterpret_cast<uintptr_t>(offs) & 7u) != 0) return KVARN_EALIGN;
+    return KVARN_OK;
+}
+
+}  // namespace
+
+// Device scratch of the entry point that allocates nothing
+// (kvarn_decode_attn_noalloc): the split-K partials of decode attention.  Each
+// GPU the library runs on holds its own copy for the life of the process.
+static __device__ __align__(256) float scratch[KVARN_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, set on first use
+
+// Device address of the current device's copy of `scratch`.  The host-side name
+// of the array is not a device address; hipGetSymbolAddress, called once per
+// device with that device current, gives it.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return KVARN_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (p == nullptr) return KVARN_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return KVARN_OK;
 }
 
@@ -144,12 +178,17 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
     return (size_t)batch * (size_t)n_q_heads * (size_t)n_splits * (size_t)kvarn::kDecodePart * sizeof(float);
 }
 
-int kvarn_decode_attn_windows(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
-                              const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
-                              int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale,
-                              const void* k_sink, const void* v_sink, int n_sink, const void* k_recent,
-                              const void* v_recent, const int32_t* n_recent_per_seq, int recent_cap, void* out,
-                              void* workspace, size_t workspace_bytes, int flags, hipStream_t stream) {
+}  // extern "C"
+
+// Decode attention with the caller's workspace, or (use_scratch) with the
+// library's device scratch in its place.  Every argument check comes before the
+// first HIP call.
+static int decode_impl(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
+                       const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
+                       int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, const void* k_sink,
+                       const void* v_sink, int n_sink, const void* k_recent, const void* v_recent,
+                       const int32_t* n_recent_per_seq, int recent_cap, void* out, void* workspace,
+                       size_t workspace_bytes, bool use_scratch, int flags, hipStream_t stream) {
     if (q == nullptr || k_packed == nullptr || v_packed == nullptr || n_tiles_per_seq == nullptr ||
         out == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || max_tiles < 0 || n_records < 0 ||
         n_q_heads % n_kv_heads != 0 || !valid_sm_scale(sm_scale) || !valid_flags(flags))
@@ -174,8 +213,14 @@ int kvarn_decode_attn_windows(const void* q, const void* k_packed, const void* v
         return KVARN_EALIGN;
     if (batch == 0) return KVARN_OK;
     const size_t need = kvarn_decode_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, max_tiles);
-    if (workspace == nullptr || workspace_bytes < need) return KVARN_EWORKSPACE;
-    if (!aligned16(workspace)) return KVARN_EALIGN;
+    if (use_scratch) {
+        if (need > (size_t)KVARN_NOALLOC_SCRATCH_BYTES) return KVARN_EWORKSPACE;
+        const int st = scratch_address(&workspace);      // the first HIP call
+        if (st != KVARN_OK) return st;
+    } else {
+        if (workspace == nullptr || workspace_bytes < need) return KVARN_EWORKSPACE;
+        if (!aligned16(workspace)) return KVARN_EALIGN;
+    }
     DecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.k_packed = static_cast<const uint8_t*>(k_packed);
@@ -203,6 +248,28 @@ int kvarn_decode_attn_windows(const void* q, const void* k_packed, const void* v
     a.stream = stream;
     kvarn::decode_split_plan(batch, n_kv_heads, n_q_heads, max_tiles, &a.n_splits, &a.tiles_per_split);
     return hip_status(kvarn::launch_decode(a));
+}
+
+extern "C" {
+
+int kvarn_decode_attn_windows(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
+                              const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
+                              int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale,
+                              const void* k_sink, const void* v_sink, int n_sink, const void* k_recent,
+                              const void* v_recent, const int32_t* n_recent_per_seq, int recent_cap, void* out,
+                              void* workspace, size_t workspace_bytes, int flags, hipStream_t stream) {
+    return decode_impl(q, k_packed, v_packed, block_table, n_tiles_per_seq, n_records, batch, n_q_heads, n_kv_heads,
+                       max_tiles, bits_k, bits_v, sm_scale, k_sink, v_sink, n_sink, k_recent, v_recent,
+                       n_recent_per_seq, recent_cap, out, workspace, workspace_bytes, false, flags, stream);
+}
+
+int kvarn_decode_attn_noalloc(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,
+                              const int32_t* n_tiles_per_seq, int64_t n_records, int64_t batch, int n_q_heads,
+                              int n_kv_heads, int max_tiles, int bits_k, int bits_v, float sm_scale, void* out,
+                              int flags, hipStream_t stream) {
+    return decode_impl(q, k_packed, v_packed, block_table, n_tiles_per_seq, n_records, batch, n_q_heads, n_kv_heads,
+                       max_tiles, bits_k, bits_v, sm_scale, nullptr, nullptr, 0, nullptr, nullptr, nullptr, 0, out,
+                       nullptr, 0, true, flags, stream);
 }
 
 int kvarn_decode_attn(const void* q, const void* k_packed, const void* v_packed, const int32_t* block_table,

@@ -33,7 +33,9 @@ SIGNATURES = {
     "kvarn_decode_attn": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _I, _P]),
     "kvarn_decode_attn_windows": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _P,
                                        _I, _P, _P, _SZ, _I, _P]),
+    "kvarn_decode_attn_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _P, _I, _P]),
 }
+NOALLOC_SCRATCH_BYTES = 16 << 20   # KVARN_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -249,4 +251,29 @@ def decode_attn(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
                                           _ptr(k_recent), _ptr(v_recent), _ptr(n_recent, torch.int32), cap, _ptr(out),
                                           _ptr(workspace), ws_bytes, flags, _stream(stream))
     _check("kvarn_decode_attn_windows", st)
+    return out
+
+
+def decode_attn_noalloc(q: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
+                        n_tiles_per_seq: torch.Tensor, n_kv_heads: int, max_tiles: int, bits_k: int, bits_v: int, *,
+                        out: torch.Tensor, block_table: torch.Tensor | None = None, sm_scale: float | None = None,
+                        flags: int = 0, stream=None) -> torch.Tensor:
+    """kvarn_decode_attn_noalloc: decode attention with the library's device
+    scratch in place of a workspace.  ``out`` (fp16, like q) is the caller's; the
+    call allocates nothing, here or in the library."""
+    _need(q.dim() == 3 and q.shape[2] == HEAD_DIM and q.dtype == torch.float16, "q: fp16 [batch][n_q_heads][128]")
+    batch, n_q_heads, _ = q.shape
+    _nbytes(q, "q")
+    _need(out.shape == q.shape and out.dtype == torch.float16 and out.is_contiguous(), "out: contiguous, like q")
+    if sm_scale is None:
+        sm_scale = HEAD_DIM ** -0.5
+    _check_index(n_tiles_per_seq, batch, "n_tiles_per_seq", torch.int32)
+    _check_index(block_table, batch * n_kv_heads * max(max_tiles, 0), "block_table", torch.int32)
+    tbk, tbv = tile_bytes(bits_k), tile_bytes(bits_v)
+    n_records = min(_nbytes(k_packed, "k_packed") // tbk, _nbytes(v_packed, "v_packed") // tbv) if tbk and tbv else 0
+    st = load().kvarn_decode_attn_noalloc(_ptr(q), _ptr(k_packed), _ptr(v_packed), _ptr(block_table, torch.int32),
+                                          _ptr(n_tiles_per_seq, torch.int32), n_records, batch, n_q_heads, n_kv_heads,
+                                          max_tiles, bits_k, bits_v, float(sm_scale), _ptr(out), flags,
+                                          _stream(stream))
+    _check("kvarn_decode_attn_noalloc", st)
     return out

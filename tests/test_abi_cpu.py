@@ -26,7 +26,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     lib = kvarn.load()
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(kvarn.SIGNATURES) == names
@@ -125,6 +125,27 @@ def test_decode_argument_errors():
         assert da(sm=sm) == kvarn.EINVAL, sm
     for sm in (0.0, -0.088, 2.0 ** 32, 2.0 ** -32):
         assert da(b=0, sm=sm) == kvarn.OK, sm
+
+
+def test_decode_noalloc_argument_errors():
+    """kvarn_decode_attn_noalloc checks its arguments as kvarn_decode_attn does
+    and refuses a shape that needs more than the library's scratch, all before
+    any HIP call."""
+    lib = kvarn.load()
+
+    def dn(qp=A, nt=A, b=2, hq=8, hkv=2, mt=4, bk=2, sm=0.088, fl=0):
+        return lib.kvarn_decode_attn_noalloc(qp, A, A, None, nt, 10, b, hq, hkv, mt, bk, 2, sm, A2, fl, None)
+
+    assert dn(qp=None) == kvarn.EINVAL
+    assert dn(nt=None) == kvarn.EINVAL
+    assert dn(hq=6, hkv=4) == kvarn.EINVAL
+    assert dn(bk=3) == kvarn.EUNSUPPORTED
+    assert dn(qp=MIS) == kvarn.EALIGN
+    assert dn(fl=8) == kvarn.EINVAL
+    assert dn(sm=float("nan")) == kvarn.EINVAL
+    assert dn(b=0) == kvarn.OK
+    assert kvarn.workspace_bytes(256, 128, 8, 64) > kvarn.NOALLOC_SCRATCH_BYTES
+    assert dn(b=256, hq=128, hkv=8, mt=64) == kvarn.EWORKSPACE
 
 
 def test_decode_workspace_plan():
