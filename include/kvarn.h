@@ -107,12 +107,23 @@ enum { KVARN_AXIS_K = 0, KVARN_AXIS_V = 1 };
  *                      KIVI baseline of its appendix I); s2 is then the constant
  *                      1/2 of the power-of-two gauge, exact, so codes, s1 and z
  *                      are those of textbook min-max RTN scaled by 2.
+ *   KVARN_SINGLE_SCALE read side only (dequantise and decode), together with
+ *                      KVARN_NO_ROTATION, for KIVI records (written with
+ *                      KVARN_NO_ROTATION and n_iter = 0, whose s2 is 1/2 at
+ *                      every index): the kernels neither read the s2 block nor
+ *                      apply a second scale per element, but fold the constant
+ *                      1/2 into s1 and z -- the single-scale dequantisation of
+ *                      the KIVI baseline that the pages time against KVarN's
+ *                      fused dual-scale one (paperlayer.ai summary, appendix I).
+ *                      Results equal those without the flag bit for bit on
+ *                      such records; on any other record they are wrong.  With
+ *                      quantise, or without KVARN_NO_ROTATION, KVARN_EINVAL.
  * Rotation with n_iter = 0 is the Hadamard-only (QuaRot-style) variant the
  * pages compare against (agihunt.info note, results table).  A record does not
  * carry its variant: dequantise and decode it with the flags it was written
  * with.  Unknown flag bits are KVARN_EINVAL.
  */
-enum { KVARN_NO_ROTATION = 1 };
+enum { KVARN_NO_ROTATION = 1, KVARN_SINGLE_SCALE = 2 };
 
 /* Version of the packed record layout described above. */
 int kvarn_format_version(void);

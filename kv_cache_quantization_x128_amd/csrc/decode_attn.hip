@@ -236,7 +236,10 @@ struct WaveSmem {
     uint2 kmeta[64], vmeta[64];  // metadata blocks of the tile pair being computed
 };
 
-template <int BK, int BV, bool ROT>
+// DUAL = false (KVARN_SINGLE_SCALE, KIVI records only): the s2 blocks are not
+// read (the lanes that would load them load s1 again, a line already being
+// fetched) and the records' constant s2 = 1/2 stands in for them.
+template <int BK, int BV, bool ROT, bool DUAL>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ n_tiles_per_seq, int64_t n_records,
@@ -282,8 +285,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         const __amdgpu_buffer_rsrc_t rv = record_rsrc(vp + (ok ? idx : 0) * RV::kBytes, ok ? RV::kBytes : 0);
         load_codes<BK>(rk, lane, t.kc);
         load_codes<BV>(rv, lane, t.vc);
-        t.km = ld8(rk, RK::kS1 + 8 * lane);
-        t.vm = ld8(rv, RV::kS1 + 8 * lane);
+        const int moff = (DUAL || (lane >> 4) != 1) ? 8 * lane : 8 * (lane - 16);   // lanes 16-31: s2
+        t.km = ld8(rk, RK::kS1 + moff);
+        t.vm = ld8(rv, RV::kS1 + moff);
     };
     TileRaw ta, tb;
     int64_t ia = record_of(j0), ib;
@@ -383,7 +387,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         float sc[8];
         {
             float s2[8];
-            fp8x8(*reinterpret_cast<const uint2*>(km + 128 + 8 * n), s2);
+            if constexpr (DUAL) {
+                fp8x8(*reinterpret_cast<const uint2*>(km + 128 + 8 * n), s2);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s2[i] = 0.5f;
+            }
             v4f d[8];   // eight independent products, issued back to back
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
@@ -433,7 +442,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         // ---- values: channels 8n + blk for query qg
         {
             float s2[8];
-            fp8x8(*reinterpret_cast<const uint2*>(vm + 128 + 8 * n), s2);
+            if constexpr (DUAL) {
+                fp8x8(*reinterpret_cast<const uint2*>(vm + 128 + 8 * n), s2);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s2[i] = 0.5f;
+            }
             v4f d[8];
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
@@ -635,12 +649,12 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     }
 }
 
-template <int BK, int BV, bool ROT>
+template <int BK, int BV, bool ROT, bool DUAL>
 hipError_t launch_bits(const DecodeArgs& a) {
     const int gs = a.n_q_heads / a.n_kv_heads;
     const int n_chunks = (gs + 3) / 4;
     const dim3 grid((unsigned)((a.n_splits + 3) / 4), (unsigned)(a.n_kv_heads * n_chunks), (unsigned)a.batch);
-    decode_mfma_kernel<BK, BV, ROT><<<grid, dim3(256), 0, a.stream>>>(
+    decode_mfma_kernel<BK, BV, ROT, DUAL><<<grid, dim3(256), 0, a.stream>>>(
         a.q, a.k_packed, a.v_packed, a.block_table, a.n_tiles_per_seq, a.n_records, a.n_q_heads, a.n_kv_heads,
         a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace,
         Windows{a.k_sink, a.v_sink, a.n_sink, a.k_recent, a.v_recent, a.n_recent, a.recent_cap});
@@ -653,7 +667,8 @@ hipError_t launch_bits(const DecodeArgs& a) {
 
 template <int BK, int BV>
 hipError_t launch_bits(const DecodeArgs& a) {
-    return a.rotate ? launch_bits<BK, BV, true>(a) : launch_bits<BK, BV, false>(a);
+    if (a.rotate) return launch_bits<BK, BV, true, true>(a);   // the API allows single scale only unrotated
+    return a.dual ? launch_bits<BK, BV, false, true>(a) : launch_bits<BK, BV, false, false>(a);
 }
 
 }  // namespace

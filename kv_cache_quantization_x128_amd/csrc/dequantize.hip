@@ -186,9 +186,10 @@ struct RawRec {
 // it is used: left to itself the scheduler sinks the s2 load (of the K side)
 // to its first use after the rotation, and the wave then waits a full memory
 // latency there.
-template <int BITS, int AXIS>
+template <int BITS, int AXIS, bool DUAL>
 __device__ __forceinline__ void load_rec(const uint8_t* __restrict__ rec, int row0, int cg, RawRec& r) {
     using R = Rec<BITS>;
+    r.s2b = make_uint2(0u, 0u);   // not read without the second scale (DUAL = false)
     if constexpr (BITS == 2 && AXIS == kAxisV) {
         // 2-bit V: rows 8cg + 2q and 8cg + 2q + 1 of every token quarter h of
         // the lane's tokens lie in the 16-byte chunk 1024 q + 16 (16 (row0 / 32)
@@ -202,7 +203,7 @@ __device__ __forceinline__ void load_rec(const uint8_t* __restrict__ rec, int ro
         const int g0 = row0, x0 = 8 * cg;
         r.s1b = *reinterpret_cast<const uint2*>(rec + R::kS1 + g0);
         r.zb = *reinterpret_cast<const uint4*>(rec + R::kZ + 2 * g0);
-        r.s2b = *reinterpret_cast<const uint2*>(rec + R::kS2 + x0);
+        if constexpr (DUAL) r.s2b = *reinterpret_cast<const uint2*>(rec + R::kS2 + x0);
         __builtin_amdgcn_sched_barrier(0);   // keep every load above this point
         // piece of quarter h: row 2q in bits 0-15, row 2q + 1 in bits 16-31
         uint32_t p0 = __builtin_amdgcn_perm(c.z, c.x, 0x05040100u), p1 = __builtin_amdgcn_perm(c.z, c.x, 0x07060302u);
@@ -235,11 +236,15 @@ __device__ __forceinline__ void load_rec(const uint8_t* __restrict__ rec, int ro
     const int x0 = (AXIS == kAxisK) ? row0 : 8 * cg;   // s2 indices of the block
     r.s1b = *reinterpret_cast<const uint2*>(rec + R::kS1 + g0);
     r.zb = *reinterpret_cast<const uint4*>(rec + R::kZ + 2 * g0);
-    r.s2b = *reinterpret_cast<const uint2*>(rec + R::kS2 + x0);
+    if constexpr (DUAL) r.s2b = *reinterpret_cast<const uint2*>(rec + R::kS2 + x0);
     __builtin_amdgcn_sched_barrier(0);   // keep every load above this point
 }
 
-template <int BITS, int AXIS, int ODT, bool ROT>
+// DUAL = false (KVARN_SINGLE_SCALE, KIVI records only): no s2 block is read and
+// no second scale is applied per element; the records' constant s2 = 1/2 is
+// folded into s1 and z (exact), which leaves the single-scale RTN
+// dequantisation  code * s1' + z'  of one FMA per element.
+template <int BITS, int AXIS, int ODT, bool ROT, bool DUAL>
 __global__ __launch_bounds__(256, 5) void dequantize_kernel(const uint8_t* __restrict__ packed,
                                                          const int64_t* __restrict__ src_index,
                                                          void* __restrict__ out, int64_t tile_stride,
@@ -255,12 +260,17 @@ __global__ __launch_bounds__(256, 5) void dequantize_kernel(const uint8_t* __res
     // matrix-core kernel below does, measured 4 % slower here.)
     const int64_t start = dst_off ? dst_off[tile] : tile * tile_stride;
     RawRec raw;
-    load_rec<BITS, AXIS>(packed + (src_index ? src_index[tile] : tile) * (int64_t)R::kBytes, row0, cg, raw);
+    load_rec<BITS, AXIS, DUAL>(packed + (src_index ? src_index[tile] : tile) * (int64_t)R::kBytes, row0, cg, raw);
     // metadata of the block: per-channel (8cg..) and per-token (row0..) vectors
     float s1v[8], zv[8], s2v[8];
     fp8x8(raw.s1b, s1v);
     f16x8(raw.zb, zv);
-    fp8x8(raw.s2b, s2v);
+    if constexpr (DUAL) {
+        fp8x8(raw.s2b, s2v);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s1v[k] *= 0.5f, zv[k] *= 0.5f, s2v[k] = 1.0f;
+    }
     float c[8][8];   // c[a][j]: token row0 + a, channel 8cg + j
     {
         float t[8][8];
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(256, 5) void dequantize_kernel(const uint8_t* __res
         for (int a = 0; a < 8; ++a)
 #pragma unroll
             for (int j = 0; j < 8; ++j) c[a][j] = fmaf(c[a][j], a1[j], a0[j]);
-    } else {
+    } else if constexpr (DUAL) {
         float m2[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) m2[j] = sg * nrm * s2v[j];
@@ -291,6 +301,11 @@ __global__ __launch_bounds__(256, 5) void dequantize_kernel(const uint8_t* __res
         for (int a = 0; a < 8; ++a)
 #pragma unroll
             for (int j = 0; j < 8; ++j) c[a][j] = fmaf(c[a][j], s1v[a], zv[a]) * m2[j];
+    } else {
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[a][j] = fmaf(c[a][j], s1v[a], zv[a]);
     }
     // inverse rotation over the 128 channels of every token
     if (rotate) {
@@ -307,7 +322,7 @@ __global__ __launch_bounds__(256, 5) void dequantize_kernel(const uint8_t* __res
 #pragma unroll
         for (int a = 0; a < 8; ++a) KVARN_FMAC_DPP8(c[a], s4, "row_half_mirror");
     }
-    if constexpr (AXIS == kAxisK) {
+    if constexpr (AXIS == kAxisK && DUAL) {
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
             const float f = s2v[a] * nrm;
@@ -497,10 +512,10 @@ __global__ __launch_bounds__(256) void dequantize_k_mfma_kernel(const uint8_t* _
     store_segs8<ODT>(out, e, ((start | token_stride) & 7) == 0, c);
 }
 
-template <int BITS, int AXIS, bool ROT>
+template <int BITS, int AXIS, bool ROT, bool DUAL>
 hipError_t launch_bits_axis(const DequantizeArgs& a) {
     const dim3 g((unsigned)a.n_tiles), block(256);
-    if constexpr (AXIS == kAxisK && ROT) {
+    if constexpr (AXIS == kAxisK && ROT && DUAL) {
         switch (a.out_dtype) {
         case kF16:
             dequantize_k_mfma_kernel<BITS, kF16><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
@@ -519,15 +534,15 @@ hipError_t launch_bits_axis(const DequantizeArgs& a) {
     }
     switch (a.out_dtype) {
     case kF16:
-        dequantize_kernel<BITS, AXIS, kF16, ROT><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
+        dequantize_kernel<BITS, AXIS, kF16, ROT, DUAL><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
                                                                         a.token_stride, a.dst_offset);
         break;
     case kBF16:
-        dequantize_kernel<BITS, AXIS, kBF16, ROT><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
+        dequantize_kernel<BITS, AXIS, kBF16, ROT, DUAL><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
                                                                          a.token_stride, a.dst_offset);
         break;
     default:
-        dequantize_kernel<BITS, AXIS, kF32, ROT><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
+        dequantize_kernel<BITS, AXIS, kF32, ROT, DUAL><<<g, block, 0, a.stream>>>(a.packed, a.src_index, a.out, a.tile_stride,
                                                                         a.token_stride, a.dst_offset);
         break;
     }
@@ -536,7 +551,8 @@ hipError_t launch_bits_axis(const DequantizeArgs& a) {
 
 template <int BITS, int AXIS>
 hipError_t launch_bits_axis(const DequantizeArgs& a) {
-    return a.rotate ? launch_bits_axis<BITS, AXIS, true>(a) : launch_bits_axis<BITS, AXIS, false>(a);
+    if (a.rotate) return launch_bits_axis<BITS, AXIS, true, true>(a);   // the API allows single scale only unrotated
+    return a.dual ? launch_bits_axis<BITS, AXIS, false, true>(a) : launch_bits_axis<BITS, AXIS, false, false>(a);
 }
 
 }  // namespace

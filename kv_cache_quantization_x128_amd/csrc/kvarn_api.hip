@@ -28,7 +28,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool valid_bits(int b) { return b == 2 || b == 4; }
 bool valid_dtype(int d) { return d == KVARN_F16 || d == KVARN_BF16 || d == KVARN_F32; }
 bool valid_axis(int a) { return a == KVARN_AXIS_K || a == KVARN_AXIS_V; }
-bool valid_flags(int f) { return (f & ~KVARN_NO_ROTATION) == 0; }
+// Flags of a read (dequantise, decode): KVARN_SINGLE_SCALE only with KVARN_NO_ROTATION.
+bool valid_flags(int f) {
+    if ((f & ~(KVARN_NO_ROTATION | KVARN_SINGLE_SCALE)) != 0) return false;
+    return !(f & KVARN_SINGLE_SCALE) || (f & KVARN_NO_ROTATION);
+}
+// Flags of quantise: the variant the records are written as.
+bool valid_write_flags(int f) { return (f & ~KVARN_NO_ROTATION) == 0; }
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return KVARN_OK;
@@ -114,7 +120,7 @@ int kvarn_quantize_tiles(const void* x, int x_dtype, int64_t n_tiles, int64_t ti
                          const int64_t* tile_offset, int bits, int axis, int n_iter, void* packed,
                          const int64_t* dst_tile_index, int flags, hipStream_t stream) {
     if (!valid_dtype(x_dtype) || !valid_axis(axis) || packed == nullptr || n_iter < 0 || n_iter > 64 ||
-        !valid_flags(flags))
+        !valid_write_flags(flags))
         return KVARN_EINVAL;
     if (!valid_bits(bits)) return KVARN_EUNSUPPORTED;
     const int st = check_tiles(x, n_tiles, tile_stride, token_stride, tile_offset);
@@ -153,7 +159,7 @@ int kvarn_dequantize_tiles(const void* packed, const int64_t* src_tile_index, in
         DequantizeArgs a{pb, src_tile_index ? src_tile_index + base : nullptr, std::min(kTilesPerLaunch, n_tiles - base),
                          bits, axis, ob, out_dtype, tile_stride, token_stride,
                          dst_tile_offset ? dst_tile_offset + base : nullptr, (flags & KVARN_NO_ROTATION) ? 0 : 1,
-                         stream};
+                         (flags & KVARN_SINGLE_SCALE) ? 0 : 1, stream};
         const int r = hip_status(kvarn::launch_dequantize(a));
         if (r != KVARN_OK) return r;
     }
@@ -238,6 +244,7 @@ static int decode_impl(const void* q, const void* k_packed, const void* v_packed
     a.out = static_cast<uint16_t*>(out);
     a.workspace = static_cast<float*>(workspace);
     a.rotate = (flags & KVARN_NO_ROTATION) ? 0 : 1;
+    a.dual = (flags & KVARN_SINGLE_SCALE) ? 0 : 1;
     a.k_sink = has_sink && n_sink > 0 ? static_cast<const uint16_t*>(k_sink) : nullptr;
     a.v_sink = has_sink && n_sink > 0 ? static_cast<const uint16_t*>(v_sink) : nullptr;
     a.n_sink = has_sink ? n_sink : 0;

@@ -29,6 +29,7 @@ struct DequantizeArgs {
     int64_t tile_stride, token_stride;
     const int64_t* dst_offset;
     int rotate;
+    int dual;                   // 0 with KVARN_SINGLE_SCALE: s2 is the constant 1/2, not read
     hipStream_t stream;
 };
 
@@ -49,6 +50,7 @@ struct DecodeArgs {
     float* workspace;
     int n_splits, tiles_per_split;
     int rotate;
+    int dual;                               // 0 with KVARN_SINGLE_SCALE
     const uint16_t *k_sink, *v_sink;        // FP16 windows (null: absent)
     int n_sink;
     const uint16_t *k_recent, *v_recent;

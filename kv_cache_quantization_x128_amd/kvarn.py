@@ -18,6 +18,7 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 F16, BF16, F32 = 0, 1, 2
 AXIS_K, AXIS_V = 0, 1
 NO_ROTATION = 1          # flag: the variant without the Walsh-Hadamard rotation (KIVI with n_iter = 0)
+SINGLE_SCALE = 2         # read flag, with NO_ROTATION: KIVI records dequantised without a second scale
 HEAD_DIM = TILE = 128
 
 # Every function declared in include/kvarn.h, with its ctypes signature.

@@ -63,7 +63,8 @@ def test_quantize_argument_errors():
     assert q(tok=132) == kvarn.EALIGN
     assert q(ts=16388) == kvarn.EALIGN
     assert q(off=P(0x10004)) == kvarn.EALIGN
-    assert q(fl=2) == kvarn.EINVAL and q(fl=-1) == kvarn.EINVAL  # unknown variant flags
+    assert q(fl=-1) == kvarn.EINVAL and q(fl=4) == kvarn.EINVAL   # unknown variant flags
+    assert q(fl=kvarn.SINGLE_SCALE | kvarn.NO_ROTATION, it=0) == kvarn.EINVAL   # a read-side flag
     assert q(n=0) == kvarn.OK  # empty batch: a no-op that touches no device
     assert q(n=0, fl=kvarn.NO_ROTATION, it=0) == kvarn.OK
 
@@ -83,6 +84,8 @@ def test_dequantize_argument_errors():
     assert dq(fl=4) == kvarn.EINVAL
     assert dq(n=0) == kvarn.OK
     assert dq(n=0, fl=kvarn.NO_ROTATION) == kvarn.OK
+    assert dq(n=0, fl=kvarn.NO_ROTATION | kvarn.SINGLE_SCALE) == kvarn.OK
+    assert dq(n=0, fl=kvarn.SINGLE_SCALE) == kvarn.EINVAL     # single scale only for unrotated (KIVI) records
 
 
 def da(qp=A, k=A, v=A, bt=None, nt=A, nrec=10, b=2, hq=8, hkv=2, mt=4, bk=2, bv=2, out=A2, ws=A, wsb=1 << 20,
@@ -121,6 +124,8 @@ def test_decode_argument_errors():
     assert da(b=0) == kvarn.OK
     assert da(fl=8) == kvarn.EINVAL
     assert da(b=0, fl=kvarn.NO_ROTATION) == kvarn.OK
+    assert da(b=0, fl=kvarn.NO_ROTATION | kvarn.SINGLE_SCALE) == kvarn.OK
+    assert da(b=0, fl=kvarn.SINGLE_SCALE) == kvarn.EINVAL
     for sm in (float("nan"), float("inf"), 2.0 ** 33, -(2.0 ** 33), 2.0 ** -33):
         assert da(sm=sm) == kvarn.EINVAL, sm
     for sm in (0.0, -0.088, 2.0 ** 32, 2.0 ** -32):

@@ -375,3 +375,30 @@ def test_streaming_cache_block_fill(dev):
     check("end")
     # the pool holds exactly the quantised blocks, in fill order
     assert next_record == sum((L - n_sink) // cap for L in lengths) * hkv
+
+
+@pytest.mark.parametrize("bk,bv", [(2, 2), (4, 2)])
+def test_single_scale_decode_of_kivi_records(dev, bk, bv):
+    """Decode attention with KVARN_SINGLE_SCALE over KIVI records equals the
+    dual-scale path bit for bit (the records' s2 is the constant 1/2) and the
+    oracle within the bar."""
+    batch, hkv, gs, max_tiles = 3, 2, 4, 5
+    hq = gs * hkv
+    rng = np.random.default_rng(61 + bk)
+    n_rec = batch * hkv * max_tiles
+    kx = (rng.standard_normal((n_rec, 128, 128)) * np.exp(rng.normal(0, 0.5, (n_rec, 1, 128)))).astype(np.float16)
+    vx = rng.standard_normal((n_rec, 128, 128)).astype(np.float16)
+    kr = oracle.quantize(oracle.TileView.dense(tiles_bits(kx), oracle.DT_F16), bk, K, n_iter=0, rotate=False)
+    vr = oracle.quantize(oracle.TileView.dense(tiles_bits(vx), oracle.DT_F16), bv, V, n_iter=0, rotate=False)
+    q = rng.standard_normal((batch, hq, 128)).astype(np.float16)
+    n_tiles = np.array([5, 2, 0], np.int32)
+    d = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    dual = kvarn.decode_attn(d(q), d(kr), d(vr), d(n_tiles), hkv, max_tiles, bk, bv, flags=kvarn.NO_ROTATION)
+    single = kvarn.decode_attn(d(q), d(kr), d(vr), d(n_tiles), hkv, max_tiles, bk, bv,
+                               flags=kvarn.NO_ROTATION | kvarn.SINGLE_SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(dual, single)
+    ref = oracle.decode_attn(q.view(np.uint16), kr, vr, n_tiles, hq, hkv, max_tiles, bk, bv, rotate=False)
+    err = parity.rel_l2_rows(single.float().cpu().numpy()[:2], ref[:2])
+    _log("single scale", bk, bv, "max rel l2", err.max())
+    assert err.max() <= TOL

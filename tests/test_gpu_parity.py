@@ -436,3 +436,25 @@ def test_phi4_full_size(dev):
         del rec
     del k, v
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------------- single scale
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("axis", [K, V])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_single_scale_dequant_of_kivi_records(dev, bits, axis, dtype):
+    """KVARN_SINGLE_SCALE on KIVI records (no rotation, no normalisation: s2 is
+    1/2 everywhere) skips the s2 block and the per-element second scale and
+    gives, bit for bit, what the dual-scale path gives; both match the oracle."""
+    k, v = synth.tiny(seed=1012, n_tokens=2048)
+    x = tiles_bits(k if axis == K else v)
+    rec = oracle.quantize(oracle.TileView.dense(x, oracle.DT_F16), bits, axis, n_iter=0, rotate=False)
+    assert (oracle.record_fields(rec, bits)[2] == 0x30).all()          # s2 = 1/2 (FP8 0x30)
+    rd = torch.from_numpy(rec).to(dev)
+    dual = kvarn.dequantize(rd, bits, axis, dtype, flags=kvarn.NO_ROTATION)
+    single = kvarn.dequantize(rd, bits, axis, dtype, flags=kvarn.NO_ROTATION | kvarn.SINGLE_SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(dual.view(torch.uint8), single.view(torch.uint8))
+    if dtype == torch.float32:
+        err = parity.dequant_fp32_error(single.cpu().numpy(), oracle.dequantize(rec, bits, axis, rotate=False))
+        assert err < 1e-3
