@@ -476,9 +476,31 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         if (ib >= 0) compute(tb);
     }
 
+    // ---- the wave's accumulator back in the channel domain: acc H / sqrt(128)
+    // (the query's 16-lane network; lane n ends with channels 8 out_group(n)..+7,
+    // sign kWhtSigma).  Without the rotation the lane keeps channels 8n..8n+7.
+    const int oc = rotate ? out_group(n) : n;          // first channel / 8 of the lane's output
+    if (rotate) {
+        fwht_regs<8>(acc);
+        const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
+        const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(dpp<kDppXor1>(acc[i]), s1, acc[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(dpp<kDppXor2>(acc[i]), s2, acc[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(dpp<0x128>(acc[i]), s3, acc[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(dpp<kDppHalfMirror>(acc[i]), s4, acc[i]);
+        const float sg = mask_sign(kWhtSigma, n) * kInvSqrtN;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= sg;
+    }
+
     // ---- FP16 sink and recent windows: this wave's share of their tokens, in
-    // the channel domain with the unrotated query (exact fp32 products), then
-    // moved into the rotated domain of acc.  Chunks of 8 tokens share one
+    // the channel domain (exact fp32 products), each lane on its output channels
+    // 8 oc..8 oc + 7 -- the dot products run over all 16 lanes of a query row,
+    // so the channel order does not matter.  Chunks of 8 tokens share one
     // rescale of the running accumulators.
     const int nr = win.k_recent ? min(max(win.n_recent[b], 0), win.recent_cap) : 0;
     const int n_sink = win.k_sink ? win.n_sink : 0;
@@ -491,12 +513,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
             auto tok_ptr = [&](const uint16_t* sink, const uint16_t* recent, int u) -> const uint4* {
                 const uint16_t* p = u < n_sink ? sink + (hkv_row * n_sink + u) * kN
                                                : recent + (hkv_row * win.recent_cap + (u - n_sink)) * kN;
-                return reinterpret_cast<const uint4*>(p + 8 * n);
+                return reinterpret_cast<const uint4*>(p + 8 * oc);
             };
-            float qp[8], accp[8];
-            f16x8(qraw, qp);
+            float qp[8];
+            uint4 qc = make_uint4(0u, 0u, 0u, 0u);
+            if (q_ok) qc = *reinterpret_cast<const uint4*>(q + ((b * n_q_heads + hq) * kN + 8 * oc));
+            f16x8(qc, qp);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qp[i] *= scale_log2, accp[i] = 0.0f;
+            for (int i = 0; i < 8; ++i) qp[i] *= scale_log2;
             for (int c0 = u0; c0 < u1; c0 += 8) {
                 uint4 kr[8], vr[8];
 #pragma unroll
@@ -522,7 +546,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                 float ps = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] *= alpha, accp[i] *= alpha;
+                for (int i = 0; i < 8; ++i) acc[i] *= alpha;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const float pt = __builtin_amdgcn_exp2f(sc[t] - m_new);
@@ -530,123 +554,63 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
                     f16x8(vr[t], vv);
                     ps += pt;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) accp[i] = fmaf(pt, vv[i], accp[i]);
+                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(pt, vv[i], acc[i]);
                 }
                 l_run = fmaf(l_run, alpha, ps);
                 m_run = m_new;
             }
-            if (rotate) {
-                // accp H / sqrt(128): the query's 16-lane network leaves group
-                // out_group(n) (sign kWhtSigma) in lane n; acc's lane m holds
-                // group m, read from lane out_group(m)
-                fwht_regs<8>(accp);
-                const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
-                const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) accp[i] = fmaf(dpp<kDppXor1>(accp[i]), s1, accp[i]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) accp[i] = fmaf(dpp<kDppXor2>(accp[i]), s2, accp[i]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) accp[i] = fmaf(dpp<0x128>(accp[i]), s3, accp[i]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) accp[i] = fmaf(dpp<kDppHalfMirror>(accp[i]), s4, accp[i]);
-                const int src = 16 * qg + out_group(n);
-                const float sgn = mask_sign(kWhtSigma, out_group(n)) * kInvSqrtN;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    acc[i] = fmaf(__int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(accp[i]))), sgn,
-                                  acc[i]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += accp[i];
-            }
         }
     }
 
-    // ---- this wave's partial: m, l, acc[channels 8n..8n+7] of query qg
+    // ---- this wave's partial: m, l, acc[channels 8 oc..8 oc + 7] of query qg
     if (q_ok) {
         float* dst = ws + ((b * n_q_heads + hq) * n_splits + split) * kPart;
         if (n == 0) dst[0] = m_run, dst[1] = l_run;
-        float4* a = reinterpret_cast<float4*>(dst + kAcc + 8 * n);
+        float4* a = reinterpret_cast<float4*>(dst + kAcc + 8 * oc);
         a[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         a[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
 }
 
-// One wave per (sequence, KV head, chunk of 4 query heads): log-sum-exp merge
-// of the splits, inverse rotation (the same 16-lane Hadamard network as the
-// query rotation), FP16.  Lane = (query qg, channels 8n..8n+7).
-template <bool ROT>
+// One wave per (sequence, query head): log-sum-exp merge of the splits'
+// partials, which the decode kernel has already rotated back into the channel
+// domain, and FP16 output.  Lane l holds channels 2l and 2l + 1; every lane reads
+// the (m, l) pair of each split (one cache line per split).  The splits are
+// taken eight at a time, all of their loads issued before any is used.
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws, int n_splits,
-                                                            int n_q_heads, int n_kv_heads, int gs, int n_chunks,
                                                             uint16_t* __restrict__ out) {
-    constexpr bool rotate = ROT;
-    const int lane = threadIdx.x, qg = lane >> 4, n = lane & 15;
-    const int chunk = blockIdx.x % n_chunks, kvh = (blockIdx.x / n_chunks) % n_kv_heads;
-    const int64_t b = blockIdx.x / (n_chunks * n_kv_heads);
-    const int hq = kvh * gs + 4 * chunk + qg;
-    const bool q_ok = 4 * chunk + qg < gs;
-    const float* p = ws + (b * n_q_heads + (q_ok ? hq : kvh * gs)) * (int64_t)n_splits * kPart;
-    // every load of a group of 16 splits is issued before any is used: lane n of
-    // a query row reads (m, l) of split c0 + n and the lane's acc slices of all
-    // 16 (indices clamped into range; slots past the last split get weight 0)
-    float M = -INFINITY, L = 0.0f, a[8];
+    constexpr int kU = 8;
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;                  // b * n_q_heads + hq
+    const float* p = ws + row * (int64_t)n_splits * kPart;
+    float M = -INFINITY, L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    for (int s0 = 0; s0 < n_splits; s0 += kU) {
+        float2 ml[kU], x[kU];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = 0.0f;
-    for (int c0 = 0; c0 < n_splits; c0 += 16) {
-        const int last = min(16, n_splits - c0) - 1;
-        const float2 ml = *reinterpret_cast<const float2*>(p + (c0 + min(n, last)) * kPart);
-        const float* pc = p + c0 * kPart + kAcc + 8 * n;
-        float4 x[16][2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int si = min(i, last);
-            x[i][0] = *reinterpret_cast<const float4*>(pc + si * kPart);
-            x[i][1] = *reinterpret_cast<const float4*>(pc + si * kPart + 4);
+        for (int i = 0; i < kU; ++i) {
+            const int si = min(s0 + i, n_splits - 1);
+            ml[i] = *reinterpret_cast<const float2*>(p + (int64_t)si * kPart);
+            x[i] = *reinterpret_cast<const float2*>(p + (int64_t)si * kPart + kAcc + 2 * lane);
         }
-        const float ms = n <= last ? ml.x : -INFINITY;
-        const float m_new = fmaxf(M, row_max16(ms));
-        if (m_new == -INFINITY) continue;                // no tokens so far in this query row
-        const float alpha = exp2f(M - m_new);            // 0 on the first group with tokens
-        const float fm = ms == -INFINITY ? 0.0f : exp2f(ms - m_new);
-        L = fmaf(L, alpha, row_sum16(ml.y * fm));
+        float mc = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kU; ++i) mc = fmaxf(mc, s0 + i < n_splits ? ml[i].x : -INFINITY);
+        const float m_new = fmaxf(M, mc);
+        if (m_new == -INFINITY) continue;            // no tokens so far (uniform across the wave)
+        const float alpha = exp2f(M - m_new);        // 0 on the first group with tokens
+        L *= alpha, a0 *= alpha, a1 *= alpha;
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            const float f = (s0 + i < n_splits && ml[i].x != -INFINITY) ? exp2f(ml[i].x - m_new) : 0.0f;
+            L = fmaf(ml[i].y, f, L);
+            a0 = fmaf(x[i].x, f, a0);
+            a1 = fmaf(x[i].y, f, a1);
+        }
         M = m_new;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) a[k] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float f = __shfl(fm, 16 * qg + i);
-            a[0] = fmaf(x[i][0].x, f, a[0]), a[1] = fmaf(x[i][0].y, f, a[1]);
-            a[2] = fmaf(x[i][0].z, f, a[2]), a[3] = fmaf(x[i][0].w, f, a[3]);
-            a[4] = fmaf(x[i][1].x, f, a[4]), a[5] = fmaf(x[i][1].y, f, a[5]);
-            a[6] = fmaf(x[i][1].z, f, a[6]), a[7] = fmaf(x[i][1].w, f, a[7]);
-        }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] *= inv;
-    if (rotate) {
-        fwht_regs<8>(a);
-        const float s1 = mask_sign(kWhtS1, n), s2 = mask_sign(kWhtS2, n);
-        const float s3 = mask_sign(kWhtS3, n), s4 = mask_sign(kWhtS4, n);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppXor1>(a[i]), s1, a[i]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppXor2>(a[i]), s2, a[i]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<0x128>(a[i]), s3, a[i]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = fmaf(dpp<kDppHalfMirror>(a[i]), s4, a[i]);
-    }
-    if (q_ok) {
-        const float sg = rotate ? mask_sign(kWhtSigma, n) * kInvSqrtN : 1.0f;
-        uint32_t h[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            h[k] = f32_to_f16_bits_sat(a[2 * k] * sg) | (f32_to_f16_bits_sat(a[2 * k + 1] * sg) << 16);
-        const int og = rotate ? out_group(n) : n;
-        *reinterpret_cast<uint4*>(out + (b * n_q_heads + hq) * kN + 8 * og) = make_uint4(h[0], h[1], h[2], h[3]);
-    }
+    reinterpret_cast<uint32_t*>(out + row * kN)[lane] =
+        f32_to_f16_bits_sat(a0 * inv) | (f32_to_f16_bits_sat(a1 * inv) << 16);
 }
 
 template <int BK, int BV, bool ROT, bool DUAL>
@@ -659,9 +623,8 @@ hipError_t launch_bits(const DecodeArgs& a) {
         a.max_tiles, a.tiles_per_split, a.n_splits, gs, n_chunks, a.sm_scale * kLog2e, a.workspace,
         Windows{a.k_sink, a.v_sink, a.n_sink, a.k_recent, a.v_recent, a.n_recent, a.recent_cap});
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    const int n_groups = (int)(a.batch * a.n_kv_heads * n_chunks);
-    decode_combine_kernel<ROT><<<dim3((unsigned)n_groups), dim3(64), 0, a.stream>>>(
-        a.workspace, a.n_splits, a.n_q_heads, a.n_kv_heads, gs, n_chunks, a.out);
+    decode_combine_kernel<<<dim3((unsigned)(a.batch * a.n_q_heads)), dim3(64), 0, a.stream>>>(a.workspace,
+                                                                                            a.n_splits, a.out);
     return hipGetLastError();
 }
 
@@ -674,8 +637,12 @@ hipError_t launch_bits(const DecodeArgs& a) {
 }  // namespace
 
 // Split-K plan: tiles of one (sequence, KV head) are cut into n_splits ranges
-// of tiles_per_split tiles, one wave each, aiming at about 4 waves per CU
-// (one per SIMD): longer splits amortise the pipeline start and the merge.
+// of tiles_per_split tiles, one wave each, aiming at one wave per SIMD (1024
+// waves on the 256 CUs): longer splits amortise the pipeline start and the
+// merge.  The split count is rounded down, never up: a grid just above 1024
+// waves leaves its last workgroups for a second round on a few CUs, and the
+// kernel then takes twice as long (the Phi-4 shape, 80 heads x 13 splits =
+// 1040 waves, did).
 void decode_split_plan(int64_t batch, int n_kv_heads, int n_q_heads, int max_tiles, int* n_splits,
                        int* tiles_per_split) {
     if (max_tiles <= 0) {
@@ -685,7 +652,7 @@ void decode_split_plan(int64_t batch, int n_kv_heads, int n_q_heads, int max_til
     }
     const int gs = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 1;
     const int64_t heads = batch * (int64_t)n_kv_heads * ((gs + 3) / 4);
-    int64_t want = heads > 0 ? (1024 + heads - 1) / heads : 1;
+    int64_t want = heads > 0 ? 1024 / heads : 1;
     if (want < 1) want = 1;
     if (want > max_tiles) want = max_tiles;
     const int tps = (int)((max_tiles + want - 1) / want);
