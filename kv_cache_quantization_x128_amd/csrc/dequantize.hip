@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256, 5) void dequantize_kernel(const uint8_t* __res
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int rg = lane >> 4, cg = lane & 15;
     const int row0 = 32 * w + 8 * rg;                 // first token of the lane's block
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     // destination first: its uniform branch placed after the compute would
     // drag the s2 load down with it.  (Loading the arguments at entry, as the
     // matrix-core kernel below does, measured 4 % slower here.)
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256) void dequantize_k_mfma_kernel(const uint8_t* _
     const int g = lane >> 4, n = lane & 15;
     const int og = out_group(n);
     KVARN_ARGS_AT_ENTRY("s"(packed), "s"(src_index), "s"(out), "s"(tile_stride), "s"(token_stride), "s"(dst_off));
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t start = dst_off ? dst_off[tile] : tile * tile_stride;
     const uint8_t* rec = packed + (src_index ? src_index[tile] : tile) * (int64_t)R::kBytes;
 
