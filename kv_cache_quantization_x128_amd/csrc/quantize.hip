@@ -236,7 +236,11 @@ __device__ __forceinline__ float step_factor(float var, float thr, float floor2,
 // LDS scratch of one workgroup.
 struct Smem {
     float4 xch[2][4][64];   // cross-wave partials, double-buffered
-    float4 col[4][16][4];   // per wave: (f, f^2) of the 8 columns of each channel group
+    // per wave: (f, f^2) of the 8 columns of each channel group; the fifth float4
+    // pads a group to 80 bytes, so that the 16 groups of a read or write fall on
+    // 16 disjoint sets of 4 banks (at 64 bytes, groups g and g + 4 shared banks:
+    // 640 conflict cycles per wave, 5 % of the kernel's time)
+    float4 col[4][16][5];
     float4 row[4][4][4];    // per wave: (f, f^2) of the 8 rows of each row group
     float gsum[4];          // per wave: gauge partial sums
 };
