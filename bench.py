@@ -655,11 +655,11 @@ def cpu_baseline(sample, n_full, min_s=10.0, max_passes=12):
             "extrapolation": f"the whole headline step ({n_full} K + {n_full} V tiles) at the sample's rate"}
 
 
-def cpu_decode_layer(n_seq_sample=4, batch=16, hq=32, hkv=8, tokens=32768):
-    """The oracle's decode attention on a slice of one layer of the Qwen3-4B
-    decode workload (n_seq_sample of the batch's sequences, all their KV heads
-    and tiles; records written by the oracle itself, untimed), extrapolated to
-    the whole layer."""
+def cpu_decode_layer(n_seq_sample=16, batch=16, hq=32, hkv=8, tokens=32768):
+    """The oracle's decode attention on one layer of the Qwen3-4B decode
+    workload (by default all of the batch's sequences, KV heads and tiles;
+    records written by the oracle itself, untimed); a slice of n_seq_sample
+    sequences is extrapolated to the whole layer."""
     import oracle
 
     g = synth.generator(1005, "cpu")
@@ -674,8 +674,10 @@ def cpu_decode_layer(n_seq_sample=4, batch=16, hq=32, hkv=8, tokens=32768):
     dt = time.perf_counter() - t0
     return {"layer_s": dt * batch / n_seq_sample, "unit": "s per layer", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{n_seq_sample} of {batch} sequences x {hkv} KV heads x {tokens} tokens (2-bit K and V), "
-                      f"{dt:.1f} s on the host, extrapolated to the layer's {batch} sequences"}
+            "sample": (f"the whole layer: {batch} sequences x {hkv} KV heads x {tokens} tokens (2-bit K and V), "
+                       f"{dt:.1f} s on the host" if n_seq_sample == batch else
+                       f"{n_seq_sample} of {batch} sequences x {hkv} KV heads x {tokens} tokens (2-bit K and V), "
+                       f"{dt:.1f} s on the host, extrapolated to the layer's {batch} sequences")}
 
 
 def pages_context(variants, q_ms, layers=36):
