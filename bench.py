@@ -554,7 +554,9 @@ def bench_decode(passes, warmup, layers=36, batch=16, hq=32, hkv=8, tokens=32768
         "fp16_equiv_GBs": 2 * batch * hkv * nt * TILE_F16_BYTES / (layer_ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("decode_mfma") if (bk, bv, batch, hq, hkv, tokens) == (2, 2, 16, 32, 8, 32768) else None,
+                     "traffic": ({(2, 2, 16, 32, 8, 32768): lambda: measured_traffic("decode_mfma"),
+                                  (4, 2, 8, 40, 10, 16384): lambda: measured_traffic("decode_mfma", "phi4")}
+                                 .get((bk, bv, batch, hq, hkv, tokens), lambda: None)()),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "tokens_per_s": batch * hq / (layer_ms * 1e-3),
     }
