@@ -458,3 +458,50 @@ def test_single_scale_dequant_of_kivi_records(dev, bits, axis, dtype):
     if dtype == torch.float32:
         err = parity.dequant_fp32_error(single.cpu().numpy(), oracle.dequantize(rec, bits, axis, rotate=False))
         assert err < 1e-3
+
+
+# ------------------------------------------------------------------------------------- launch split
+def test_batches_beyond_one_launch(dev):
+    """A call of more than 2^23 tiles runs as consecutive launches.  2^23 + 3
+    tiles whose offsets cycle over 7 distinct input tiles: the records on both
+    sides of the split equal the records of their input tiles bit for bit, and
+    those pass the comparison protocol against the oracle; dequantising all of
+    them through a source index into destination offsets (record i into slot
+    i % 7) gives the oracle's dequantisation of the 7 records.  With the
+    identity layouts (tile_stride 0, no index) the records past the split equal
+    the first, and so do their dequantisations.  About 39 GB of records."""
+    n = (1 << 23) + 3
+    split = 1 << 23
+    k, _ = synth.tiny(seed=1013, n_tokens=7 * 128)
+    x = torch.from_numpy(k).to(dev).view(7, 128, 128)
+    per = 128 * 128
+    offs = (torch.arange(n, device=dev, dtype=torch.int64) % 7) * per
+    packed = torch.empty((n, kvarn.tile_bytes(2)), dtype=torch.uint8, device=dev)
+    _log("launch split: quantise", n, "tiles through offsets")
+    kvarn.quantize_tiles(x, n, 2, K, tile_offset=offs, out=packed)
+    torch.cuda.synchronize()
+    first = packed[:7].cpu().numpy()
+    rep = parity.compare_quantize(oracle.TileView.dense(tiles_bits(k), oracle.DT_F16), 2, K, first)
+    _log(rep)
+    parity.assert_quantize_parity(rep)
+    edge = torch.arange(split - 7, n, device=dev)
+    assert torch.equal(packed[edge], packed[edge % 7])
+    out = torch.empty((7, 128, 128), dtype=torch.float32, device=dev)
+    src = torch.arange(n, device=dev, dtype=torch.int64)
+    _log("launch split: dequantise through a source index into 7 slots")
+    kvarn.dequantize_tiles(packed, n, 2, K, out, src_index=src, dst_offset=offs)
+    torch.cuda.synchronize()
+    err = parity.dequant_fp32_error(out.cpu().numpy(), oracle.dequantize(first, 2, K))
+    _log("dequant max err / tile rms", err)
+    assert err < 1e-3
+    del src, offs
+    _log("launch split: identity layouts, tile_stride 0")
+    kvarn.quantize_tiles(x, n, 2, K, tile_stride=0, out=packed)
+    one = torch.empty((1, 128, 128), dtype=torch.float32, device=dev)
+    kvarn.dequantize_tiles(packed, n, 2, K, one, tile_stride=0)
+    torch.cuda.synchronize()
+    assert torch.equal(packed[split - 1:], packed[:1].expand(4, -1))
+    ref = oracle.dequantize(packed[:1].cpu().numpy(), 2, K)
+    assert parity.dequant_fp32_error(one.cpu().numpy(), ref) < 1e-3
+    del packed
+    torch.cuda.empty_cache()
