@@ -24,9 +24,10 @@
 //       matrix core sums the pieces in fp32.  The representation error of x is
 //       at most 2^-16 (scores) or 2^-12 (weights) of |x|.
 // Every wave owns a range of tiles of one (sequence, KV head, 4-query chunk)
-// and keeps its own running max, sum and accumulator (flash-decoding); the
-// waves' partials are merged by a second kernel that also applies the inverse
-// rotation and rounds to FP16.
+// and keeps its own running max, sum and accumulator (flash-decoding); it
+// rotates its accumulator back to the channel domain before writing its
+// partial, and a second kernel merges the waves' partials (log-sum-exp) and
+// rounds to FP16.
 #include "kvarn_device.h"
 #include "kvarn_launch.h"
 
