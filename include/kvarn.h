@@ -212,8 +212,10 @@ size_t kvarn_decode_attn_workspace_bytes(int64_t batch, int n_q_heads, int n_kv_
  *                   query heads of one KV head are taken in chunks of 4, each
  *                   chunk reading that head's records once.  batch at most
  *                   65535, and n_kv_heads times the number of chunks per KV
- *                   head, ceil(n_q_heads / n_kv_heads / 4), at most 65535
- *                   (KVARN_EUNSUPPORTED otherwise)
+ *                   head, ceil(n_q_heads / n_kv_heads / 4), at most 65535,
+ *                   and batch * n_q_heads below 2^26 (the merge runs one
+ *                   64-thread workgroup per output row) (KVARN_EUNSUPPORTED
+ *                   otherwise)
  *   bits_k, bits_v  2 or 4
  *   sm_scale        softmax scale, 1/sqrt(128) for standard attention; zero or
  *                   2^-32 <= |sm_scale| <= 2^32 (KVARN_EINVAL otherwise)

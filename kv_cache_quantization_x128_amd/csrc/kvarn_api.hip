@@ -207,8 +207,11 @@ static int decode_impl(const void* q, const void* k_packed, const void* v_packed
                        recent_cap > 65536))
         return KVARN_EINVAL;
     if (!valid_bits(bits_k) || !valid_bits(bits_v)) return KVARN_EUNSUPPORTED;
-    // grid limits: z = batch, y = n_kv_heads x chunks of 4 query heads
-    if (batch > 65535 || (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 3) / 4) > 65535) return KVARN_EUNSUPPORTED;
+    // grid limits: z = batch, y = n_kv_heads x chunks of 4 query heads; the merge
+    // runs one 64-thread workgroup per (sequence, query head), fewer than 2^32 threads
+    if (batch > 65535 || (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 3) / 4) > 65535 ||
+        batch * (int64_t)n_q_heads * 64 > (int64_t)UINT32_MAX)
+        return KVARN_EUNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_packed) || !aligned16(v_packed) || !aligned16(out)) return KVARN_EALIGN;
     if ((reinterpret_cast<uintptr_t>(n_tiles_per_seq) & 3u) != 0 ||
         (block_table != nullptr && (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))

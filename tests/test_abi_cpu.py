@@ -118,6 +118,8 @@ def test_decode_argument_errors():
     assert da(bk=3) == kvarn.EUNSUPPORTED
     assert da(b=65536) == kvarn.EUNSUPPORTED                 # grid z
     assert da(hq=8 * 40000, hkv=40000) == kvarn.EUNSUPPORTED  # grid y: 40000 KV heads x 2 chunks
+    assert da(b=65535, hq=4 * 16384, hkv=16384) == kvarn.EUNSUPPORTED  # merge: 65535 x 65536 rows of 64 threads
+    assert da(b=0, hq=4 * 16384, hkv=16384) == kvarn.OK
     assert da(qp=MIS) == kvarn.EALIGN
     assert da(ws=None) == kvarn.EWORKSPACE
     assert da(wsb=16) == kvarn.EWORKSPACE
